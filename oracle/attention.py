@@ -98,8 +98,10 @@ def combine_partials(outs, lses):
     Empty parts (lse_s = -inf) carry zero weight; if every part is empty the
     result is o = 0, lse = -inf.
     """
-    outs = np.asarray(outs, np.float64)
     lses = np.asarray(lses, np.float64)
+    if lses.size == 0:                    # no parts: the empty sum
+        return np.zeros(np.shape(outs)[1:], np.float64), -np.inf
+    outs = np.asarray(outs, np.float64)
     M = np.max(lses)
     if M == -np.inf:
         return np.zeros(outs.shape[1:], np.float64), -np.inf

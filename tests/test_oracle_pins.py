@@ -344,6 +344,11 @@ def test_two_identical_halves_add_log_two():
     assert le == lse
     o0, l0 = oracle.combine_partials([np.zeros(3)], [-np.inf])
     assert np.all(o0 == 0) and l0 == -np.inf
+    # no parts at all is the attention of an empty sequence
+    oz, lz = oracle.combine_partials(np.zeros((0, 3)), np.zeros(0))
+    oa, la = oracle.attend(q, K[:0], V[:0], 1.0)
+    np.testing.assert_array_equal(oz, oa)
+    assert lz == la == -np.inf
 
 
 # ------------------------------------------------------------------------------------------------
