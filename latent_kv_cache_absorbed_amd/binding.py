@@ -1,0 +1,245 @@
+"""Python binding of the C ABI in include/latent_decode.h (ctypes; argument marshalling only).
+
+Every step of the decode runs in the gfx950 kernels of ``liblatent_decode.so``.
+This module only checks that tensors are contiguous device tensors of the
+right dtype, derives the ``ld_problem`` shape from them, allocates outputs and
+the workspace with torch when the caller does not pass them, and calls the
+library on torch's current stream.  There is no CPU fallback: if the library
+is missing, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import torch
+
+__all__ = [
+    "LatentDecodeError", "lib", "library_path", "Problem", "KVCache", "VARIANTS", "DTYPES",
+    "make_problem", "workspace_size", "latent_decode", "split_kv_combine", "validate_metadata", "plan_host",
+    "check_problem", "status_string", "header_functions",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_HERE, "liblatent_decode.so")
+HEADER = os.path.join(os.path.dirname(_HERE), "include", "latent_decode.h")
+
+VARIANTS = {"mla": 0, "gla": 1, "mlra": 2, "gqa": 3, "mqa": 4, "gta": 5}
+DTYPES = {"f32": 0, "bf16": 1, "fp8_e4m3": 2}
+_TORCH_DTYPE = {torch.float32: "f32", torch.bfloat16: "bf16", torch.uint8: "fp8_e4m3",
+                torch.float8_e4m3fn: "fp8_e4m3"}
+
+
+class LatentDecodeError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} (status {status})")
+
+
+class Problem(ctypes.Structure):
+    _fields_ = [("struct_size", ctypes.c_uint32), ("variant", ctypes.c_int32), ("batch", ctypes.c_int32),
+                ("num_q_heads", ctypes.c_int32), ("num_groups", ctypes.c_int32), ("d_latent", ctypes.c_int32),
+                ("d_rope", ctypes.c_int32), ("page_size", ctypes.c_int32), ("num_pages", ctypes.c_int32),
+                ("max_pages_per_seq", ctypes.c_int32), ("q_dtype", ctypes.c_int32), ("kv_dtype", ctypes.c_int32),
+                ("out_dtype", ctypes.c_int32), ("softmax_scale", ctypes.c_float), ("num_splits", ctypes.c_int32)]
+
+
+class KVCache(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_void_p), ("rope", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("scale", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(library_path):
+            raise RuntimeError(f"{library_path} is missing: build it with `python -m latent_kv_cache_absorbed_amd.build`")
+        L = ctypes.CDLL(library_path)
+        i32, vp, sz = ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t
+        P = ctypes.POINTER(Problem)
+        ip = ctypes.POINTER(ctypes.c_int32)
+        L.ld_abi_version.restype = i32
+        L.ld_abi_version.argtypes = []
+        L.ld_status_string.restype = ctypes.c_char_p
+        L.ld_status_string.argtypes = [i32]
+        L.ld_check_problem.restype = i32
+        L.ld_check_problem.argtypes = [P]
+        L.ld_workspace_size.restype = i32
+        L.ld_workspace_size.argtypes = [P, ctypes.POINTER(sz)]
+        L.ld_latent_decode.restype = i32
+        L.ld_latent_decode.argtypes = [P, vp, vp, ctypes.POINTER(KVCache), vp, vp, vp, vp, vp, sz, vp]
+        L.ld_split_kv_combine.restype = i32
+        L.ld_split_kv_combine.argtypes = [i32, i32, i32, vp, vp, vp, i32, vp, vp, vp]
+        L.ld_validate_metadata.restype = i32
+        L.ld_validate_metadata.argtypes = [P, ip, ip]
+        L.ld_plan_host.restype = i32
+        L.ld_plan_host.argtypes = [P, ip, i32, ip, ip, ip, ip]
+        _lib = L
+    return _lib
+
+
+def header_functions() -> list:
+    """Names of the functions include/latent_decode.h declares."""
+    with open(HEADER) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(ld_\w+)\s*\(", text, re.M)))
+
+
+def status_string(status: int) -> str:
+    try:
+        return lib().ld_status_string(int(status)).decode()
+    except RuntimeError:
+        return f"status {status}"
+
+
+def make_problem(variant: str, batch: int, heads: int, groups: int, d_latent: int, d_rope: int, page_size: int,
+                 num_pages: int, max_pages_per_seq: int, q_dtype: str, kv_dtype: str, out_dtype: str, scale: float,
+                 num_splits: int = 0) -> Problem:
+    return Problem(ctypes.sizeof(Problem), VARIANTS[variant], batch, heads, groups, d_latent, d_rope, page_size,
+                   num_pages, max_pages_per_seq, DTYPES[q_dtype], DTYPES[kv_dtype], DTYPES[out_dtype], float(scale),
+                   num_splits)
+
+
+def check_problem(p: Problem) -> int:
+    return lib().ld_check_problem(ctypes.byref(p))
+
+
+def workspace_size(p: Problem) -> int:
+    n = ctypes.c_size_t(0)
+    st = lib().ld_workspace_size(ctypes.byref(p), ctypes.byref(n))
+    if st:
+        raise LatentDecodeError(st, "ld_workspace_size")
+    return n.value
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _need(t, name, dtypes=None):
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtypes is not None and t.dtype not in dtypes:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    return t
+
+
+def latent_decode(q_latent, q_rope, k, block_table, seq_lens, *, variant: str, scale: float, groups: int | None = None,
+                  v=None, rope=None, kscale=None, out=None, lse=None, out_dtype: str | None = None,
+                  num_splits: int = 0, workspace=None, stream=None):
+    """One decode step; returns (out, lse).  Layouts as in include/latent_decode.h.
+
+    ``k`` holds the cache rows (for an fp8 latent cache: the E4M3 codes as
+    uint8 or float8_e4m3fn, with ``rope`` and ``kscale`` beside it).
+    """
+    if variant not in VARIANTS:
+        raise ValueError(f"unknown variant {variant!r}")
+    _need(q_latent, "q_latent", (torch.float32, torch.bfloat16))
+    _need(k, "k", tuple(_TORCH_DTYPE))
+    _need(block_table, "block_table", (torch.int32,))
+    _need(seq_lens, "seq_lens", (torch.int32,))
+    kv_dtype = _TORCH_DTYPE[k.dtype]
+    q_dtype = _TORCH_DTYPE[q_latent.dtype]
+    latent = variant in ("mla", "gla", "mlra")
+    B, H = q_latent.shape[0], q_latent.shape[1]
+    d = q_latent.shape[-1]
+    if latent:
+        _need(q_rope, "q_rope", (q_latent.dtype,))
+        dr = q_rope.shape[-1]
+        if variant == "mlra":
+            G = q_latent.shape[2]
+        elif variant == "mla":
+            G = 1
+        else:
+            lat_cols = k.shape[-1] if kv_dtype == "fp8_e4m3" else k.shape[-1] - dr
+            G = groups if groups is not None else lat_cols // d
+        if kv_dtype == "fp8_e4m3":
+            _need(rope, "rope", (torch.bfloat16,))
+            _need(kscale, "kscale", (torch.float32,))
+    else:
+        dr = 0
+        G = k.shape[2]
+        if variant != "gta":
+            _need(v, "v", (k.dtype,))
+    if groups is not None and groups != G:
+        raise ValueError(f"groups={groups} does not match the tensors ({G})")
+    out_dtype = out_dtype or ("f32" if q_dtype == "f32" else "bf16")
+    p = make_problem(variant, B, H, G, d, dr, k.shape[1], k.shape[0], block_table.shape[1], q_dtype, kv_dtype,
+                     out_dtype, scale, num_splits)
+    rows = H * G if variant == "mlra" else H
+    odt = torch.float32 if out_dtype == "f32" else torch.bfloat16
+    dev = q_latent.device
+    if out is None:
+        out = torch.empty((B, H, G, d) if variant == "mlra" else (B, H, d), dtype=odt, device=dev)
+    if lse is None:
+        lse = torch.empty((B, H, G) if variant == "mlra" else (B, H), dtype=torch.float32, device=dev)
+    _need(out, "out", (odt,))
+    _need(lse, "lse", (torch.float32,))
+    if out.numel() != B * rows * d or lse.numel() != B * rows:
+        raise ValueError("out/lse have the wrong size")
+    ws_bytes = workspace_size(p)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    _need(workspace, "workspace")
+    cache = KVCache(k.data_ptr(), None if rope is None else rope.data_ptr(),
+                    None if v is None else v.data_ptr(), None if kscale is None else kscale.data_ptr())
+    if stream is None:
+        stream = torch.cuda.current_stream(dev).cuda_stream
+    st = lib().ld_latent_decode(ctypes.byref(p), _ptr(q_latent), _ptr(q_rope), ctypes.byref(cache),
+                                _ptr(block_table), _ptr(seq_lens), _ptr(out), _ptr(lse), _ptr(workspace),
+                                workspace.numel() * workspace.element_size(), ctypes.c_void_p(stream))
+    if st:
+        raise LatentDecodeError(st, "ld_latent_decode")
+    return out, lse
+
+
+def split_kv_combine(partial_out, partial_lse, row_num_splits, *, out_dtype: str = "f32", out=None, lse=None,
+                     stream=None):
+    """Merge split partials: partial_out [rows, S, d_v] f32, partial_lse [rows, S] f32, row_num_splits [rows] i32."""
+    _need(partial_out, "partial_out", (torch.float32,))
+    _need(partial_lse, "partial_lse", (torch.float32,))
+    _need(row_num_splits, "row_num_splits", (torch.int32,))
+    rows, S, dv = partial_out.shape
+    odt = torch.float32 if out_dtype == "f32" else torch.bfloat16
+    if out is None:
+        out = torch.empty((rows, dv), dtype=odt, device=partial_out.device)
+    if lse is None:
+        lse = torch.empty((rows,), dtype=torch.float32, device=partial_out.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(partial_out.device).cuda_stream
+    st = lib().ld_split_kv_combine(rows, dv, S, _ptr(partial_out), _ptr(partial_lse), _ptr(row_num_splits),
+                                   DTYPES[out_dtype], _ptr(out), _ptr(lse), ctypes.c_void_p(stream))
+    if st:
+        raise LatentDecodeError(st, "ld_split_kv_combine")
+    return out, lse
+
+
+def validate_metadata(p: Problem, block_table_host, seq_lens_host) -> int:
+    bt = torch.as_tensor(block_table_host, dtype=torch.int32).contiguous()
+    sl = torch.as_tensor(seq_lens_host, dtype=torch.int32).contiguous()
+    ip = ctypes.POINTER(ctypes.c_int32)
+    return lib().ld_validate_metadata(ctypes.byref(p), ctypes.cast(bt.data_ptr(), ip), ctypes.cast(sl.data_ptr(), ip))
+
+
+def plan_host(p: Problem, seq_lens_host, num_cus: int):
+    """Host planner: returns (chunk, num_units, splits[B], first_unit[B])."""
+    sl = torch.as_tensor(seq_lens_host, dtype=torch.int32).contiguous()
+    B = p.batch
+    splits = torch.zeros(max(B, 1), dtype=torch.int32)
+    first = torch.zeros(max(B, 1), dtype=torch.int32)
+    chunk, units = ctypes.c_int32(0), ctypes.c_int32(0)
+    ip = ctypes.POINTER(ctypes.c_int32)
+    st = lib().ld_plan_host(ctypes.byref(p), ctypes.cast(sl.data_ptr(), ip), num_cus, ctypes.byref(chunk),
+                            ctypes.byref(units), ctypes.cast(splits.data_ptr(), ip), ctypes.cast(first.data_ptr(), ip))
+    if st:
+        raise LatentDecodeError(st, "ld_plan_host")
+    return chunk.value, units.value, splits[:B].numpy().copy(), first[:B].numpy().copy()

@@ -1,0 +1,314 @@
+// Host side of the C ABI: problem checks, workspace layout, the host copy of the split-KV
+// planner, and the launch sequence plan -> decode -> combine.  See include/latent_decode.h.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "ld_internal.h"
+
+namespace ld {
+namespace {
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
+bool latent(const ld_problem& p) { return p.variant <= LD_VARIANT_MLRA; }
+
+int elem_bytes_lds(int kv) { return kv == LD_F32 ? 4 : 2; }  // fp8 is staged as bf16
+
+struct Shape {
+  int heads_per_set = 0, hblocks = 0, nsets = 0, wg_per_unit = 0;
+};
+
+// Sets per work group: the largest of 8, 4, 2, 1 that divides G and whose waves and LDS
+// tile fit the kernel built for this shape.
+Shape launch_shape(const ld_problem& p) {
+  Shape s;
+  const int H = p.num_q_heads, G = p.num_groups;
+  s.heads_per_set = p.variant == LD_VARIANT_MLRA ? H : H / G;
+  s.hblocks = (s.heads_per_set + 31) / 32;
+  const int es = elem_bytes_lds(p.kv_dtype);
+  for (int n = 8; n >= 1; n >>= 1) {
+    if (n > kernel_max_sets(p) || G % n) continue;
+    if (n * s.hblocks * kWaveSize > kernel_max_threads(p)) continue;
+    size_t lds = (size_t)kTile * ((size_t)(n * p.d_latent + p.d_rope) * es);
+    if (p.variant == LD_VARIANT_GQA || p.variant == LD_VARIANT_MQA) lds += (size_t)kTile * n * p.d_latent * es;
+    if (p.kv_dtype == LD_FP8_E4M3) lds += kTile * sizeof(float);
+    if (lds > 160 * 1024) continue;
+    s.nsets = n;
+    s.wg_per_unit = G / n;
+    break;
+  }
+  return s;
+}
+
+WsLayout ws_layout(const ld_problem& p, int num_cus) {
+  WsLayout w;
+  w.max_units = max_units_for(p, num_cus);
+  w.rows = rows_per_seq(p);
+  w.d_v = p.d_latent;
+  size_t off = 0;
+  w.header = off;
+  off += 256;
+  w.units = off;
+  off = round256(off + (size_t)w.max_units * sizeof(Unit));
+  w.seqs = off;
+  off = round256(off + (size_t)p.batch * 2 * sizeof(int32_t));
+  w.part_lse = off;
+  off = round256(off + (size_t)w.max_units * w.rows * sizeof(float));
+  w.part_out = off;
+  off = round256(off + (size_t)w.max_units * w.rows * w.d_v * sizeof(float));
+  w.total = off;
+  return w;
+}
+
+}  // namespace
+
+int32_t rows_per_seq(const ld_problem& p) {
+  return p.variant == LD_VARIANT_MLRA ? p.num_q_heads * p.num_groups : p.num_q_heads;
+}
+
+// Units the automatic planner aims for: one wave of work groups over the chip.
+int32_t target_units_for(const ld_problem& p, int32_t num_cus) {
+  const Shape s = launch_shape(p);
+  const int wpu = s.wg_per_unit > 0 ? s.wg_per_unit : 1;
+  int t = num_cus / wpu;
+  return t < 1 ? 1 : t;
+}
+
+int32_t max_units_for(const ld_problem& p, int32_t num_cus) {
+  if (p.num_splits > 0) {
+    const long long m = (long long)p.batch * p.num_splits;
+    return (int32_t)(m > (1 << 30) ? (1 << 30) : m);
+  }
+  return target_units_for(p, num_cus) + p.batch;
+}
+
+}  // namespace ld
+
+using namespace ld;
+
+extern "C" {
+
+int32_t ld_abi_version(void) { return LD_ABI_VERSION; }
+
+const char* ld_status_string(int32_t s) {
+  switch (s) {
+    case LD_OK: return "ok";
+    case LD_ERR_NULL_POINTER: return "a required pointer is NULL";
+    case LD_ERR_BAD_SHAPE: return "bad or inconsistent problem shape";
+    case LD_ERR_BAD_DTYPE: return "unsupported dtype combination";
+    case LD_ERR_MISALIGNED: return "a pointer is not aligned as required";
+    case LD_ERR_UNSUPPORTED: return "shape not supported by the built kernels";
+    case LD_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case LD_ERR_BAD_METADATA: return "block table or sequence lengths out of range";
+    case LD_ERR_HIP: return "HIP launch failed";
+    case LD_ERR_BAD_STRUCT: return "ld_problem struct_size mismatch";
+    default: return "unknown status";
+  }
+}
+
+int32_t ld_check_problem(const ld_problem* p) {
+  if (!p) return LD_ERR_NULL_POINTER;
+  if (p->struct_size != sizeof(ld_problem)) return LD_ERR_BAD_STRUCT;
+  if (p->variant < LD_VARIANT_MLA || p->variant > LD_VARIANT_GTA) return LD_ERR_BAD_SHAPE;
+  if (p->batch < 0 || p->num_q_heads < 1 || p->num_groups < 1 || p->d_latent < 1 || p->d_rope < 0)
+    return LD_ERR_BAD_SHAPE;
+  if (p->page_size < 1 || p->page_size > (1 << 20) || p->num_pages < 1 || p->max_pages_per_seq < 1)
+    return LD_ERR_BAD_SHAPE;
+  if ((long long)p->max_pages_per_seq * p->page_size > 0x7fffffffLL) return LD_ERR_BAD_SHAPE;
+  if (p->num_splits < 0) return LD_ERR_BAD_SHAPE;
+  if (!std::isfinite(p->softmax_scale)) return LD_ERR_BAD_SHAPE;
+  const int H = p->num_q_heads, G = p->num_groups;
+  switch (p->variant) {
+    case LD_VARIANT_MLA:
+    case LD_VARIANT_MQA:
+      if (G != 1) return LD_ERR_BAD_SHAPE;
+      break;
+    case LD_VARIANT_GLA:
+    case LD_VARIANT_GQA:
+    case LD_VARIANT_GTA:
+      if (H % G) return LD_ERR_BAD_SHAPE;
+      break;
+    default:
+      break;
+  }
+  if (latent(*p)) {
+    if (p->d_rope < 1) return LD_ERR_BAD_SHAPE;
+  } else if (p->d_rope != 0) {
+    return LD_ERR_BAD_SHAPE;
+  }
+  // dtypes: f32 query with f32 cache; bf16 query with bf16 or (latent) fp8 cache
+  if (p->out_dtype != LD_F32 && p->out_dtype != LD_BF16) return LD_ERR_BAD_DTYPE;
+  if (p->kv_dtype == LD_F32) {
+    if (p->q_dtype != LD_F32) return LD_ERR_BAD_DTYPE;
+  } else if (p->kv_dtype == LD_BF16) {
+    if (p->q_dtype != LD_BF16) return LD_ERR_BAD_DTYPE;
+  } else if (p->kv_dtype == LD_FP8_E4M3) {
+    if (p->q_dtype != LD_BF16 || !latent(*p)) return LD_ERR_BAD_DTYPE;
+  } else {
+    return LD_ERR_BAD_DTYPE;
+  }
+  if (!decode_supported(*p)) return LD_ERR_UNSUPPORTED;
+  if (launch_shape(*p).nsets == 0) return LD_ERR_UNSUPPORTED;
+  return LD_OK;
+}
+
+int32_t ld_workspace_size(const ld_problem* p, size_t* bytes) {
+  if (!bytes) return LD_ERR_NULL_POINTER;
+  const int32_t st = ld_check_problem(p);
+  if (st != LD_OK) return st;
+  *bytes = ws_layout(*p, device_cu_count()).total;
+  return LD_OK;
+}
+
+int32_t ld_plan_host(const ld_problem* p, const int32_t* seq_lens_host, int32_t num_cus, int32_t* chunk_out,
+                     int32_t* num_units, int32_t* splits_out, int32_t* first_unit_out) {
+  const int32_t st = ld_check_problem(p);
+  if (st != LD_OK) return st;
+  if ((p->batch > 0 && (!seq_lens_host || !splits_out || !first_unit_out)) || !chunk_out || !num_units)
+    return LD_ERR_NULL_POINTER;
+  if (num_cus < 1) return LD_ERR_BAD_SHAPE;
+  const long long cap = (long long)p->max_pages_per_seq * p->page_size;
+  const int page = p->page_size;
+  auto clampL = [&](int32_t L) -> long long { return L < 0 ? 0 : (L > cap ? cap : L); };
+  long long total = 0;
+  for (int b = 0; b < p->batch; ++b) total += clampL(seq_lens_host[b]);
+  long long chunk = 0;
+  if (p->num_splits == 0) {
+    const long long target = target_units_for(*p, num_cus);
+    const long long per = (total + target - 1) / target;
+    chunk = (per + page - 1) / page * page;
+    if (chunk < page) chunk = page;
+  }
+  long long units = 0;
+  for (int b = 0; b < p->batch; ++b) {
+    const long long L = clampL(seq_lens_host[b]);
+    long long ck = chunk;
+    if (p->num_splits > 0) {
+      const long long per = (L + p->num_splits - 1) / p->num_splits;
+      ck = (per + page - 1) / page * page;
+      if (ck < page) ck = page;
+    }
+    const long long n = (L + ck - 1) / ck;
+    splits_out[b] = (int32_t)n;
+    first_unit_out[b] = (int32_t)units;
+    units += n;
+  }
+  *chunk_out = (int32_t)chunk;
+  *num_units = (int32_t)units;
+  return LD_OK;
+}
+
+int32_t ld_validate_metadata(const ld_problem* p, const int32_t* block_table_host, const int32_t* seq_lens_host) {
+  const int32_t st = ld_check_problem(p);
+  if (st != LD_OK) return st;
+  if (p->batch == 0) return LD_OK;
+  if (!block_table_host || !seq_lens_host) return LD_ERR_NULL_POINTER;
+  const long long cap = (long long)p->max_pages_per_seq * p->page_size;
+  for (int b = 0; b < p->batch; ++b) {
+    const int32_t L = seq_lens_host[b];
+    if (L < 0 || L > cap) return LD_ERR_BAD_METADATA;
+    const int used = (int)((L + p->page_size - 1) / p->page_size);
+    for (int i = 0; i < used; ++i) {
+      const int32_t pg = block_table_host[(size_t)b * p->max_pages_per_seq + i];
+      if (pg < 0 || pg >= p->num_pages) return LD_ERR_BAD_METADATA;
+    }
+  }
+  return LD_OK;
+}
+
+int32_t ld_latent_decode(const ld_problem* p, const void* q_latent, const void* q_rope, const ld_kv_cache* cache,
+                         const int32_t* block_table, const int32_t* seq_lens, void* out, float* lse, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  const int32_t st = ld_check_problem(p);
+  if (st != LD_OK) return st;
+  if (p->batch == 0) return LD_OK;
+  const bool lat = latent(*p);
+  const bool fp8 = p->kv_dtype == LD_FP8_E4M3;
+  if (!q_latent || !cache || !cache->k || !block_table || !seq_lens || !out || !lse || !workspace)
+    return LD_ERR_NULL_POINTER;
+  if (lat && !q_rope) return LD_ERR_NULL_POINTER;
+  if (fp8 && (!cache->rope || !cache->scale)) return LD_ERR_NULL_POINTER;
+  if ((p->variant == LD_VARIANT_GQA || p->variant == LD_VARIANT_MQA) && !cache->v) return LD_ERR_NULL_POINTER;
+  if (!aligned(q_latent, 16) || (lat && !aligned(q_rope, 16)) || !aligned(cache->k, 16) || !aligned(out, 16) ||
+      !aligned(lse, 4) || !aligned(block_table, 4) || !aligned(seq_lens, 4) || !aligned(workspace, 256))
+    return LD_ERR_MISALIGNED;
+  if (cache->v && !aligned(cache->v, 16)) return LD_ERR_MISALIGNED;
+  if (fp8 && (!aligned(cache->rope, 16) || !aligned(cache->scale, 4))) return LD_ERR_MISALIGNED;
+
+  const int cus = device_cu_count();
+  const WsLayout w = ws_layout(*p, cus);
+  if (workspace_bytes < w.total) return LD_ERR_WORKSPACE_TOO_SMALL;
+  const Shape s = launch_shape(*p);
+  char* ws = static_cast<char*>(workspace);
+
+  PlanArgs pa;
+  pa.seq_lens = seq_lens;
+  pa.header = reinterpret_cast<int32_t*>(ws + w.header);
+  pa.units = reinterpret_cast<Unit*>(ws + w.units);
+  pa.seqs = reinterpret_cast<int32_t*>(ws + w.seqs);
+  pa.batch = p->batch;
+  pa.capacity = p->max_pages_per_seq * p->page_size;
+  pa.page_size = p->page_size;
+  pa.target_units = target_units_for(*p, cus);
+  pa.forced_splits = p->num_splits;
+  pa.max_units = w.max_units;
+  if (launch_plan(pa, stream) != hipSuccess) return LD_ERR_HIP;
+
+  DecodeArgs a;
+  a.q_lat = q_latent;
+  a.q_rope = q_rope;
+  a.k = cache->k;
+  a.rope = cache->rope;
+  a.v = cache->v;
+  a.kscale = cache->scale;
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  a.out = out;
+  a.lse = lse;
+  a.header = pa.header;
+  a.units = pa.units;
+  a.seqs = pa.seqs;
+  a.part_lse = reinterpret_cast<float*>(ws + w.part_lse);
+  a.part_out = reinterpret_cast<float*>(ws + w.part_out);
+  a.batch = p->batch;
+  a.heads = p->num_q_heads;
+  a.groups = p->num_groups;
+  a.heads_per_set = s.heads_per_set;
+  a.rows = w.rows;
+  a.max_pages = p->max_pages_per_seq;
+  a.num_pages = p->num_pages;
+  a.page_size = p->page_size;
+  a.nsets = s.nsets;
+  a.hblocks = s.hblocks;
+  a.wg_per_unit = s.wg_per_unit;
+  a.max_units = w.max_units;
+  a.out_bf16 = p->out_dtype == LD_BF16;
+  a.mlra = p->variant == LD_VARIANT_MLRA;
+  a.scale_log2 = p->softmax_scale * 1.4426950408889634f;
+  const int r = launch_decode(*p, a, stream);
+  if (r == -1) return LD_ERR_UNSUPPORTED;
+  if (r != hipSuccess) return LD_ERR_HIP;
+  if (launch_combine_ws(a, p->d_latent, stream) != hipSuccess) return LD_ERR_HIP;
+  return LD_OK;
+}
+
+int32_t ld_split_kv_combine(int32_t num_rows, int32_t d_v, int32_t max_splits, const float* partial_out,
+                            const float* partial_lse, const int32_t* row_num_splits, int32_t out_dtype, void* out,
+                            float* lse, void* stream) {
+  if (num_rows < 0 || d_v < 4 || (d_v % 4) != 0 || max_splits < 1) return LD_ERR_BAD_SHAPE;
+  if (out_dtype != LD_F32 && out_dtype != LD_BF16) return LD_ERR_BAD_DTYPE;
+  if (num_rows == 0) return LD_OK;
+  if (!partial_out || !partial_lse || !row_num_splits || !out || !lse) return LD_ERR_NULL_POINTER;
+  if (!aligned(partial_out, 16) || !aligned(out, out_dtype == LD_F32 ? 16 : 8) || !aligned(partial_lse, 4) ||
+      !aligned(row_num_splits, 4) || !aligned(lse, 4))
+    return LD_ERR_MISALIGNED;
+  if (launch_combine_rows(num_rows, d_v, max_splits, partial_out, partial_lse, row_num_splits,
+                          out_dtype == LD_BF16, out, lse, stream) != hipSuccess)
+    return LD_ERR_HIP;
+  return LD_OK;
+}
+
+}  // extern "C"

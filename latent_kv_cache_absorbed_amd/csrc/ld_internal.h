@@ -1,0 +1,102 @@
+// Internal definitions shared by the host API and the gfx950 kernels of the
+// decode-attention library.  Not part of the C ABI.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "latent_decode.h"
+
+namespace ld {
+
+// How a work group reads K and V.
+enum Kind : int {
+  KIND_LATENT = 0,  // MLA / GLA / MLRA: K = [latent slice | rope], V = the latent slice of the same row
+  KIND_SHARED = 1,  // GQA / MQA: K and V rows from two pools
+  KIND_TIED = 2,    // GTA: V is the K row itself
+};
+
+constexpr int kTile = 32;            // tokens per MFMA tile (one 32-row block)
+constexpr int kWaveSize = 64;
+constexpr int kPlanThreads = 1024;
+
+// Work unit record written by the planner: one (sequence, token chunk).
+struct alignas(16) Unit {
+  int32_t b;
+  int32_t t_begin;
+  int32_t t_end;
+  int32_t split;
+};
+
+// Workspace layout (byte offsets from the workspace base, each 256-aligned).
+struct WsLayout {
+  int32_t max_units = 0;
+  int32_t rows = 0;        // R: output rows per sequence
+  int32_t d_v = 0;
+  size_t header = 0;       // int32[64]: [0] num_units, [1] chunk
+  size_t units = 0;        // Unit[max_units]
+  size_t seqs = 0;         // int32[2*B]: (num_splits, first_unit) per sequence
+  size_t part_lse = 0;     // f32[max_units][R]
+  size_t part_out = 0;     // f32[max_units][R][d_v]
+  size_t total = 0;
+};
+
+// Everything the decode kernels need, passed by value.
+struct DecodeArgs {
+  const void* q_lat;
+  const void* q_rope;
+  const void* k;
+  const void* rope;      // fp8 cache: bf16 rope pool
+  const void* v;
+  const float* kscale;   // fp8 cache: per-token scale
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  void* out;
+  float* lse;
+  const int32_t* header;
+  const Unit* units;
+  const int32_t* seqs;
+  float* part_lse;
+  float* part_out;
+  int32_t batch, heads, groups, heads_per_set, rows, max_pages, num_pages, page_size;
+  int32_t nsets, hblocks;       // sets per work group, 32-head blocks per set
+  int32_t wg_per_unit;          // work groups per unit (= groups / nsets)
+  int32_t max_units;
+  int32_t out_bf16;
+  int32_t mlra;
+  float scale_log2;             // softmax_scale * log2(e)
+};
+
+struct PlanArgs {
+  const int32_t* seq_lens;
+  int32_t* header;
+  Unit* units;
+  int32_t* seqs;
+  int32_t batch;
+  int32_t capacity;       // max_pages_per_seq * page_size
+  int32_t page_size;
+  int32_t target_units;   // units the planner aims for (auto mode)
+  int32_t forced_splits;  // 0 = auto
+  int32_t max_units;
+};
+
+// Host planner rule shared (as a specification, not as code) with the device
+// planner: see plan_chunk() in api.cpp and plan_kernel in plan_combine.hip.
+int32_t target_units_for(const ld_problem& p, int32_t num_cus);
+int32_t max_units_for(const ld_problem& p, int32_t num_cus);
+int32_t rows_per_seq(const ld_problem& p);
+
+// Launchers (plan_combine.hip, decode.hip).  They return hipError_t as int.
+int launch_plan(const PlanArgs& a, void* stream);
+int launch_combine_ws(const DecodeArgs& a, int32_t d_v, void* stream);
+int launch_combine_rows(int32_t num_rows, int32_t d_v, int32_t max_splits, const float* part_out,
+                        const float* part_lse, const int32_t* nsplits, int32_t out_bf16, void* out, float* lse,
+                        void* stream);
+// Returns hipError_t, or -1 when no kernel is built for the shape.
+int launch_decode(const ld_problem& p, const DecodeArgs& a, void* stream);
+bool decode_supported(const ld_problem& p);
+int kernel_max_threads(const ld_problem& p);  // work-group size limit of the kernel built for p's shape
+int kernel_max_sets(const ld_problem& p);     // largest sets-per-work-group instantiated for p's shape
+int device_cu_count();
+
+}  // namespace ld

@@ -1,0 +1,210 @@
+// Split-KV planner and log-sum-exp combine kernels (gfx950).
+//
+// Planner rule (identical to plan_host in api.cpp, which tests compare against):
+//   L_b   = clamp(seq_lens[b], 0, capacity)
+//   auto:   chunk = max(page, roundup(ceil(sum_b L_b / target_units), page)); n_b = ceil(L_b / chunk)
+//   forced: chunk_b = max(page, roundup(ceil(L_b / splits), page));        n_b = ceil(L_b / chunk_b)
+//   units of sequence b are first_b .. first_b + n_b - 1 (first_b = exclusive prefix sum of n_b),
+//   unit first_b + s covers tokens [s * chunk_b, min(L_b, (s + 1) * chunk_b)).
+//
+// Combine rule for a row split into n parts with normalised partial outputs o_s and
+// log-sum-exps lse_s:  lse = ln sum_s exp(lse_s),  o = sum_s exp(lse_s - lse) o_s.
+#include <hip/hip_runtime.h>
+
+#include "ld_internal.h"
+
+namespace ld {
+namespace {
+
+__device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
+
+__global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
+  __shared__ long long red[kPlanThreads / 64];
+  __shared__ int scan[kPlanThreads];
+  __shared__ int s_chunk;
+  __shared__ int s_carry;
+  const int tid = threadIdx.x;
+  const int page = a.page_size;
+
+  long long part = 0;
+  for (int b = tid; b < a.batch; b += blockDim.x) part += clampi(a.seq_lens[b], 0, a.capacity);
+  for (int off = 32; off > 0; off >>= 1) part += __shfl_xor(part, off);
+  if ((tid & 63) == 0) red[tid >> 6] = part;
+  __syncthreads();
+  if (tid == 0) {
+    long long total = 0;
+    for (int w = 0; w < (int)(blockDim.x >> 6); ++w) total += red[w];
+    int chunk = 0;
+    if (a.forced_splits <= 0) {
+      const long long per = (total + a.target_units - 1) / a.target_units;
+      long long c = (per + page - 1) / page * page;
+      if (c < page) c = page;
+      chunk = (int)(c > 0x7fffffffLL ? 0x7fffffff : c);
+    }
+    s_chunk = chunk;
+    s_carry = 0;
+  }
+  __syncthreads();
+  const int chunk = s_chunk;
+
+  for (int base = 0; base < a.batch; base += blockDim.x) {
+    const int b = base + tid;
+    int L = 0, ck = chunk, n = 0;
+    if (b < a.batch) {
+      L = clampi(a.seq_lens[b], 0, a.capacity);
+      if (a.forced_splits > 0) {
+        const int per = (L + a.forced_splits - 1) / a.forced_splits;
+        ck = (per + page - 1) / page * page;
+        if (ck < page) ck = page;
+      }
+      n = (L + ck - 1) / ck;
+    }
+    scan[tid] = n;
+    __syncthreads();
+    for (int off = 1; off < (int)blockDim.x; off <<= 1) {
+      const int v = tid >= off ? scan[tid - off] : 0;
+      __syncthreads();
+      scan[tid] += v;
+      __syncthreads();
+    }
+    const int first = s_carry + scan[tid] - n;
+    if (b < a.batch) {
+      a.seqs[2 * b] = n;
+      a.seqs[2 * b + 1] = first;
+      for (int s = 0; s < n; ++s) {
+        const int u = first + s;
+        if (u < a.max_units) {
+          Unit rec;
+          rec.b = b;
+          rec.t_begin = s * ck;
+          rec.t_end = min(L, (s + 1) * ck);
+          rec.split = s;
+          a.units[u] = rec;
+        }
+      }
+    }
+    __syncthreads();
+    if (tid == blockDim.x - 1) s_carry += scan[tid];
+    __syncthreads();
+  }
+  if (tid == 0) {
+    a.header[0] = min(s_carry, a.max_units);
+    a.header[1] = chunk;
+  }
+}
+
+// Merge split partials of every row of every sequence whose split count is not 1.
+// Work group = one sequence and `RPB` rows; one thread per (row, 4 columns).
+constexpr int kCombineThreads = 256;
+
+__global__ __launch_bounds__(kCombineThreads) void combine_ws_kernel(DecodeArgs a, int d_v, int rows_per_block) {
+  const int b = blockIdx.y;
+  int n = a.seqs[2 * b];
+  if (n == 1) return;
+  const int first = a.seqs[2 * b + 1];
+  n = max(0, min(n, a.max_units - first));  // the planner never exceeds the workspace; stay inside it regardless
+  const int c4n = d_v >> 2;
+  const int r0 = blockIdx.x * rows_per_block;
+  for (int idx = threadIdx.x; idx < rows_per_block * c4n; idx += blockDim.x) {
+    const int r = r0 + idx / c4n;
+    if (r >= a.rows) break;
+    const int c = (idx % c4n) * 4;
+    float M = -INFINITY;
+    for (int s = 0; s < n; ++s) M = fmaxf(M, a.part_lse[(size_t)(first + s) * a.rows + r]);
+    float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+    float lse = -INFINITY;
+    if (M != -INFINITY) {
+      float tot = 0.f;
+      for (int s = 0; s < n; ++s) tot += expf(a.part_lse[(size_t)(first + s) * a.rows + r] - M);
+      lse = M + logf(tot);
+      for (int s = 0; s < n; ++s) {
+        const size_t pr = (size_t)(first + s) * a.rows + r;
+        const float w = expf(a.part_lse[pr] - lse);
+        const float4 v = *reinterpret_cast<const float4*>(a.part_out + pr * d_v + c);
+        o.x += w * v.x;
+        o.y += w * v.y;
+        o.z += w * v.z;
+        o.w += w * v.w;
+      }
+    }
+    const size_t orow = (size_t)b * a.rows + r;
+    if (c == 0) a.lse[orow] = lse;
+    if (a.out_bf16) {
+      typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+      bf16x4_t v = {(__bf16)o.x, (__bf16)o.y, (__bf16)o.z, (__bf16)o.w};
+      *reinterpret_cast<bf16x4_t*>(static_cast<__bf16*>(a.out) + orow * d_v + c) = v;
+    } else {
+      *reinterpret_cast<float4*>(static_cast<float*>(a.out) + orow * d_v + c) = o;
+    }
+  }
+}
+
+__global__ __launch_bounds__(kCombineThreads) void combine_rows_kernel(int num_rows, int d_v, int max_splits,
+                                                                       const float* part_out, const float* part_lse,
+                                                                       const int32_t* nsplits, int out_bf16,
+                                                                       void* out, float* lse_out,
+                                                                       int rows_per_block) {
+  const int c4n = d_v >> 2;
+  const int r0 = blockIdx.x * rows_per_block;
+  for (int idx = threadIdx.x; idx < rows_per_block * c4n; idx += blockDim.x) {
+    const int r = r0 + idx / c4n;
+    if (r >= num_rows) break;
+    const int c = (idx % c4n) * 4;
+    const int n = clampi(nsplits[r], 0, max_splits);
+    const float* ls = part_lse + (size_t)r * max_splits;
+    float M = -INFINITY;
+    for (int s = 0; s < n; ++s) M = fmaxf(M, ls[s]);
+    float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+    float lse = -INFINITY;
+    if (M != -INFINITY) {
+      float tot = 0.f;
+      for (int s = 0; s < n; ++s) tot += expf(ls[s] - M);
+      lse = M + logf(tot);
+      for (int s = 0; s < n; ++s) {
+        const float w = expf(ls[s] - lse);
+        const float4 v = *reinterpret_cast<const float4*>(part_out + ((size_t)r * max_splits + s) * d_v + c);
+        o.x += w * v.x;
+        o.y += w * v.y;
+        o.z += w * v.z;
+        o.w += w * v.w;
+      }
+    }
+    if (c == 0) lse_out[r] = lse;
+    if (out_bf16) {
+      typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+      bf16x4_t v = {(__bf16)o.x, (__bf16)o.y, (__bf16)o.z, (__bf16)o.w};
+      *reinterpret_cast<bf16x4_t*>(static_cast<__bf16*>(out) + (size_t)r * d_v + c) = v;
+    } else {
+      *reinterpret_cast<float4*>(static_cast<float*>(out) + (size_t)r * d_v + c) = o;
+    }
+  }
+}
+
+}  // namespace
+
+int launch_plan(const PlanArgs& a, void* stream) {
+  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, static_cast<hipStream_t>(stream), a);
+  return (int)hipGetLastError();
+}
+
+int launch_combine_ws(const DecodeArgs& a, int32_t d_v, void* stream) {
+  if (a.batch == 0 || a.rows == 0) return 0;
+  const int rpb = d_v >= 256 ? 4 : 16;
+  const dim3 grid((a.rows + rpb - 1) / rpb, a.batch);
+  hipLaunchKernelGGL(combine_ws_kernel, grid, dim3(kCombineThreads), 0, static_cast<hipStream_t>(stream), a, d_v,
+                     rpb);
+  return (int)hipGetLastError();
+}
+
+int launch_combine_rows(int32_t num_rows, int32_t d_v, int32_t max_splits, const float* part_out,
+                        const float* part_lse, const int32_t* nsplits, int32_t out_bf16, void* out, float* lse,
+                        void* stream) {
+  if (num_rows == 0) return 0;
+  const int rpb = d_v >= 256 ? 4 : 16;
+  const dim3 grid((num_rows + rpb - 1) / rpb);
+  hipLaunchKernelGGL(combine_rows_kernel, grid, dim3(kCombineThreads), 0, static_cast<hipStream_t>(stream), num_rows,
+                     d_v, max_splits, part_out, part_lse, nsplits, out_bf16, out, lse, rpb);
+  return (int)hipGetLastError();
+}
+
+}  // namespace ld

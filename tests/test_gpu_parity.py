@@ -1,0 +1,140 @@
+"""GPU parity: the HIP path against the CPU fp64 oracle on seeded inputs (needs an MI355X)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from gpu_util import lse_err, row_rel_err, run_gpu, run_oracle, tolerance
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import latent_kv_cache_absorbed_amd as lkd
+    lkd.lib()          # fails loudly when the library is missing
+
+
+def _check(inp, num_splits=0, tol=None, **kw):
+    print(f"case variant={inp.variant} kv={inp.kv_dtype} H={inp.heads} G={inp.groups} d={inp.d_lat}+{inp.d_rope} "
+          f"lens={list(inp.layout.seq_lens)[:8]} splits={num_splits}", flush=True)
+    got_o, got_l = run_gpu(inp, num_splits=num_splits)
+    ref_o, ref_l = run_oracle(inp, **kw)
+    mask = ~np.isnan(ref_l)
+    tol = tolerance(inp) if tol is None else tol
+    eo = row_rel_err(got_o, ref_o, mask)
+    el = lse_err(got_l, ref_l, mask)
+    print(f"   out err {eo:.3e}  lse err {el:.3e}  tol {tol:g}", flush=True)
+    assert eo <= tol and el <= tol
+    return got_o, got_l
+
+
+# --- the tiny fp32 absorbed-MLA workload, exactly as specified (1e-5)
+def test_mla_tiny_f32_contiguous():
+    w = synth.WORKLOADS["mla_tiny_f32"]
+    _check(synth.make_workload_inputs(w))
+
+
+@pytest.mark.parametrize("splits", [0, 1, 3])
+def test_mla_tiny_f32_splits(splits):
+    w = synth.WORKLOADS["mla_tiny_f32"]
+    _check(synth.make_workload_inputs(w, seq_lens=[256, 77], shuffle=True), num_splits=splits)
+
+
+# --- MLA bf16, 128 heads, 576-dim shared rows: ragged lengths, shuffled pages, NaN-poisoned tails
+@pytest.mark.parametrize("lens", [[1, 63, 64, 65], [300, 1000, 4097], [31, 32, 33, 129]])
+def test_mla_bf16_ragged(lens):
+    inp = synth.make_inputs("mla", len(lens), 128, 1, 512, 64, lens, scale=1 / math.sqrt(192), seed=11)
+    _check(inp)
+
+
+@pytest.mark.parametrize("splits", [1, 2, 5])
+def test_mla_bf16_forced_splits(splits):
+    inp = synth.make_inputs("mla", 2, 128, 1, 512, 64, [1500, 700], scale=1 / math.sqrt(192), seed=12)
+    _check(inp, num_splits=splits)
+
+
+def test_mla_bf16_small_heads():
+    inp = synth.make_inputs("mla", 3, 16, 1, 64, 16, [100, 1, 257], scale=0.25, seed=13)
+    _check(inp)
+
+
+# --- GLA-2 (bf16 and fp8) and MLRA-4
+@pytest.mark.parametrize("kv", ["bf16", "fp8_e4m3"])
+def test_gla2(kv):
+    inp = synth.make_inputs("gla", 3, 128, 2, 256, 64, [1, 500, 1111], scale=1 / math.sqrt(192), seed=14,
+                            kv_dtype=kv)
+    _check(inp)
+
+
+def test_mla_fp8():
+    inp = synth.make_inputs("mla", 2, 128, 1, 512, 64, [600, 65], scale=1 / math.sqrt(192), seed=15,
+                            kv_dtype="fp8_e4m3")
+    _check(inp)
+
+
+def test_mlra4():
+    inp = synth.make_inputs("mlra", 2, 128, 4, 128, 64, [700, 33], scale=1 / math.sqrt(192), seed=16)
+    _check(inp)
+
+
+# --- shared-KV baselines
+@pytest.mark.parametrize("variant,groups", [("gqa", 8), ("mqa", 1), ("gta", 8)])
+def test_shared_kv(variant, groups):
+    inp = synth.make_inputs(variant, 3, 64, groups, 128, 0, [5, 300, 1025], scale=1 / math.sqrt(128), seed=17)
+    _check(inp)
+
+
+def test_shared_kv_f32():
+    inp = synth.make_inputs("gqa", 2, 16, 4, 64, 0, [90, 200], scale=0.125, seed=18, kv_dtype="f32", q_dtype="f32",
+                            out_dtype="f32")
+    _check(inp)
+
+
+# --- edge cases
+def test_empty_sequences():
+    inp = synth.make_inputs("mla", 3, 128, 1, 512, 64, [0, 70, 0], scale=1 / math.sqrt(192), seed=19)
+    o, l = _check(inp)
+    assert np.all(o[0] == 0) and np.all(o[2] == 0)
+    assert np.all(l[0] == -np.inf) and np.all(l[2] == -np.inf)
+
+
+def test_shuffled_and_identity_tables_bitwise_equal():
+    a = synth.make_inputs("mla", 2, 128, 1, 512, 64, [333, 129], scale=0.07, seed=20, shuffle=True)
+    b = synth.make_inputs("mla", 2, 128, 1, 512, 64, [333, 129], scale=0.07, seed=20, shuffle=False)
+    oa, la = run_gpu(a)
+    ob, lb = run_gpu(b)
+    assert np.array_equal(oa, ob) and np.array_equal(la, lb)
+
+
+def test_run_to_run_bitwise_deterministic():
+    inp = synth.make_inputs("gla", 2, 128, 2, 256, 64, [2000, 10], scale=0.07, seed=21, kv_dtype="fp8_e4m3")
+    o1, l1 = run_gpu(inp)
+    o2, l2 = run_gpu(inp)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+def test_split_combine_standalone():
+    import latent_kv_cache_absorbed_amd as lkd
+    import oracle
+    r = np.random.default_rng(5)
+    rows, S, dv = 37, 6, 64
+    po = r.normal(size=(rows, S, dv)).astype(np.float32)
+    pl = (r.normal(size=(rows, S)) * 3).astype(np.float32)
+    ns = r.integers(0, S + 1, size=rows).astype(np.int32)
+    pl[3, :2] = -np.inf
+    o, l = lkd.split_kv_combine(torch.from_numpy(po).cuda(), torch.from_numpy(pl).cuda(),
+                                torch.from_numpy(ns).cuda())
+    o, l = o.double().cpu().numpy(), l.double().cpu().numpy()
+    for i in range(rows):
+        eo, el = oracle.combine_partials(po[i, :ns[i]].astype(np.float64).reshape(ns[i], dv),
+                                         pl[i, :ns[i]].astype(np.float64))
+        if ns[i] == 0 or el == -np.inf:
+            assert np.all(o[i] == 0) and l[i] == -np.inf
+            continue
+        assert np.max(np.abs(o[i] - eo)) <= 1e-5 * max(1.0, np.max(np.abs(eo)))
+        assert abs(l[i] - el) <= 1e-5 * max(1.0, abs(el))
