@@ -153,6 +153,19 @@ int32_t ld_latent_decode(const ld_problem* p, const void* q_latent, const void* 
                          const ld_kv_cache* cache, const int32_t* block_table, const int32_t* seq_lens,
                          void* out, float* lse, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Stage-wise form of ld_latent_decode: ld_plan, then ld_decode_planned, then
+ * ld_combine_planned, queued on one stream in that order with the same problem
+ * shape and workspace.  The plan depends only on seq_lens and the shape, so a
+ * caller that runs several layers over the same sequences in one decode step
+ * can plan once and run decode + combine per layer.  Each stage has the
+ * argument checks, ownership and error behaviour of ld_latent_decode. */
+int32_t ld_plan(const ld_problem* p, const int32_t* seq_lens, void* workspace, size_t workspace_bytes, void* stream);
+int32_t ld_decode_planned(const ld_problem* p, const void* q_latent, const void* q_rope, const ld_kv_cache* cache,
+                          const int32_t* block_table, const int32_t* seq_lens, void* out, float* lse,
+                          void* workspace, size_t workspace_bytes, void* stream);
+int32_t ld_combine_planned(const ld_problem* p, void* out, float* lse, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
 /* Merge per-split partial results with the log-sum-exp rule (flash-decoding
  * combine).  For row r with n = row_num_splits[r] (0 <= n <= max_splits):
  *   lse_r = ln sum_{s<n} exp(partial_lse[r][s])

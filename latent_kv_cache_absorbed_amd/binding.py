@@ -16,7 +16,7 @@ import re
 import torch
 
 __all__ = [
-    "LatentDecodeError", "lib", "library_path", "Problem", "KVCache", "VARIANTS", "DTYPES",
+    "LatentDecodeError", "Decoder", "lib", "library_path", "Problem", "KVCache", "VARIANTS", "DTYPES",
     "make_problem", "workspace_size", "latent_decode", "split_kv_combine", "validate_metadata", "plan_host",
     "check_problem", "status_string", "header_functions",
 ]
@@ -73,6 +73,12 @@ def lib():
         L.ld_workspace_size.argtypes = [P, ctypes.POINTER(sz)]
         L.ld_latent_decode.restype = i32
         L.ld_latent_decode.argtypes = [P, vp, vp, ctypes.POINTER(KVCache), vp, vp, vp, vp, vp, sz, vp]
+        L.ld_plan.restype = i32
+        L.ld_plan.argtypes = [P, vp, vp, sz, vp]
+        L.ld_decode_planned.restype = i32
+        L.ld_decode_planned.argtypes = [P, vp, vp, ctypes.POINTER(KVCache), vp, vp, vp, vp, vp, sz, vp]
+        L.ld_combine_planned.restype = i32
+        L.ld_combine_planned.argtypes = [P, vp, vp, vp, sz, vp]
         L.ld_split_kv_combine.restype = i32
         L.ld_split_kv_combine.argtypes = [i32, i32, i32, vp, vp, vp, i32, vp, vp, vp]
         L.ld_validate_metadata.restype = i32
@@ -133,73 +139,118 @@ def _need(t, name, dtypes=None):
     return t
 
 
+class Decoder:
+    """A decode problem bound to its device tensors: ``run()`` is one ld_latent_decode call.
+
+    ``plan()``, ``decode()`` and ``combine()`` call the three stages separately
+    (same stream, same workspace), e.g. to plan once for several layers.
+    Layouts as in include/latent_decode.h; ``k`` holds the cache rows (for an
+    fp8 latent cache: the E4M3 codes as uint8 or float8_e4m3fn, with ``rope``
+    and ``kscale`` beside it).
+    """
+
+    def __init__(self, q_latent, q_rope, k, block_table, seq_lens, *, variant: str, scale: float,
+                 groups: int | None = None, v=None, rope=None, kscale=None, out=None, lse=None,
+                 out_dtype: str | None = None, num_splits: int = 0, workspace=None):
+        if variant not in VARIANTS:
+            raise ValueError(f"unknown variant {variant!r}")
+        _need(q_latent, "q_latent", (torch.float32, torch.bfloat16))
+        _need(k, "k", tuple(_TORCH_DTYPE))
+        _need(block_table, "block_table", (torch.int32,))
+        _need(seq_lens, "seq_lens", (torch.int32,))
+        kv_dtype = _TORCH_DTYPE[k.dtype]
+        q_dtype = _TORCH_DTYPE[q_latent.dtype]
+        latent = variant in ("mla", "gla", "mlra")
+        B, H = q_latent.shape[0], q_latent.shape[1]
+        d = q_latent.shape[-1]
+        if latent:
+            _need(q_rope, "q_rope", (q_latent.dtype,))
+            dr = q_rope.shape[-1]
+            if variant == "mlra":
+                G = q_latent.shape[2]
+            elif variant == "mla":
+                G = 1
+            else:
+                lat_cols = k.shape[-1] if kv_dtype == "fp8_e4m3" else k.shape[-1] - dr
+                G = groups if groups is not None else lat_cols // d
+            if kv_dtype == "fp8_e4m3":
+                _need(rope, "rope", (torch.bfloat16,))
+                _need(kscale, "kscale", (torch.float32,))
+        else:
+            dr = 0
+            G = k.shape[2]
+            if variant != "gta":
+                _need(v, "v", (k.dtype,))
+        if groups is not None and groups != G:
+            raise ValueError(f"groups={groups} does not match the tensors ({G})")
+        out_dtype = out_dtype or ("f32" if q_dtype == "f32" else "bf16")
+        self.problem = make_problem(variant, B, H, G, d, dr, k.shape[1], k.shape[0], block_table.shape[1], q_dtype,
+                                    kv_dtype, out_dtype, scale, num_splits)
+        rows = H * G if variant == "mlra" else H
+        odt = torch.float32 if out_dtype == "f32" else torch.bfloat16
+        dev = q_latent.device
+        if out is None:
+            out = torch.empty((B, H, G, d) if variant == "mlra" else (B, H, d), dtype=odt, device=dev)
+        if lse is None:
+            lse = torch.empty((B, H, G) if variant == "mlra" else (B, H), dtype=torch.float32, device=dev)
+        _need(out, "out", (odt,))
+        _need(lse, "lse", (torch.float32,))
+        if out.numel() != B * rows * d or lse.numel() != B * rows:
+            raise ValueError("out/lse have the wrong size")
+        ws_bytes = workspace_size(self.problem)
+        if workspace is None:
+            workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+        _need(workspace, "workspace")
+        self.cache = KVCache(k.data_ptr(), None if rope is None else rope.data_ptr(),
+                             None if v is None else v.data_ptr(), None if kscale is None else kscale.data_ptr())
+        # keep every tensor alive for as long as the pointers are used
+        self.tensors = (q_latent, q_rope, k, v, rope, kscale, block_table, seq_lens)
+        self.q_latent, self.q_rope, self.block_table, self.seq_lens = q_latent, q_rope, block_table, seq_lens
+        self.out, self.lse, self.workspace = out, lse, workspace
+        self.ws_bytes = workspace.numel() * workspace.element_size()
+        self.device = dev
+
+    def _stream(self, stream):
+        return ctypes.c_void_p(torch.cuda.current_stream(self.device).cuda_stream if stream is None else stream)
+
+    def plan(self, stream=None):
+        st = lib().ld_plan(ctypes.byref(self.problem), _ptr(self.seq_lens), _ptr(self.workspace), self.ws_bytes,
+                           self._stream(stream))
+        if st:
+            raise LatentDecodeError(st, "ld_plan")
+
+    def decode(self, stream=None):
+        st = lib().ld_decode_planned(ctypes.byref(self.problem), _ptr(self.q_latent), _ptr(self.q_rope),
+                                     ctypes.byref(self.cache), _ptr(self.block_table), _ptr(self.seq_lens),
+                                     _ptr(self.out), _ptr(self.lse), _ptr(self.workspace), self.ws_bytes,
+                                     self._stream(stream))
+        if st:
+            raise LatentDecodeError(st, "ld_decode_planned")
+
+    def combine(self, stream=None):
+        st = lib().ld_combine_planned(ctypes.byref(self.problem), _ptr(self.out), _ptr(self.lse),
+                                      _ptr(self.workspace), self.ws_bytes, self._stream(stream))
+        if st:
+            raise LatentDecodeError(st, "ld_combine_planned")
+
+    def run(self, stream=None):
+        st = lib().ld_latent_decode(ctypes.byref(self.problem), _ptr(self.q_latent), _ptr(self.q_rope),
+                                    ctypes.byref(self.cache), _ptr(self.block_table), _ptr(self.seq_lens),
+                                    _ptr(self.out), _ptr(self.lse), _ptr(self.workspace), self.ws_bytes,
+                                    self._stream(stream))
+        if st:
+            raise LatentDecodeError(st, "ld_latent_decode")
+        return self.out, self.lse
+
+
 def latent_decode(q_latent, q_rope, k, block_table, seq_lens, *, variant: str, scale: float, groups: int | None = None,
                   v=None, rope=None, kscale=None, out=None, lse=None, out_dtype: str | None = None,
                   num_splits: int = 0, workspace=None, stream=None):
-    """One decode step; returns (out, lse).  Layouts as in include/latent_decode.h.
-
-    ``k`` holds the cache rows (for an fp8 latent cache: the E4M3 codes as
-    uint8 or float8_e4m3fn, with ``rope`` and ``kscale`` beside it).
-    """
-    if variant not in VARIANTS:
-        raise ValueError(f"unknown variant {variant!r}")
-    _need(q_latent, "q_latent", (torch.float32, torch.bfloat16))
-    _need(k, "k", tuple(_TORCH_DTYPE))
-    _need(block_table, "block_table", (torch.int32,))
-    _need(seq_lens, "seq_lens", (torch.int32,))
-    kv_dtype = _TORCH_DTYPE[k.dtype]
-    q_dtype = _TORCH_DTYPE[q_latent.dtype]
-    latent = variant in ("mla", "gla", "mlra")
-    B, H = q_latent.shape[0], q_latent.shape[1]
-    d = q_latent.shape[-1]
-    if latent:
-        _need(q_rope, "q_rope", (q_latent.dtype,))
-        dr = q_rope.shape[-1]
-        if variant == "mlra":
-            G = q_latent.shape[2]
-        elif variant == "mla":
-            G = 1
-        else:
-            lat_cols = k.shape[-1] if kv_dtype == "fp8_e4m3" else k.shape[-1] - dr
-            G = groups if groups is not None else lat_cols // d
-        if kv_dtype == "fp8_e4m3":
-            _need(rope, "rope", (torch.bfloat16,))
-            _need(kscale, "kscale", (torch.float32,))
-    else:
-        dr = 0
-        G = k.shape[2]
-        if variant != "gta":
-            _need(v, "v", (k.dtype,))
-    if groups is not None and groups != G:
-        raise ValueError(f"groups={groups} does not match the tensors ({G})")
-    out_dtype = out_dtype or ("f32" if q_dtype == "f32" else "bf16")
-    p = make_problem(variant, B, H, G, d, dr, k.shape[1], k.shape[0], block_table.shape[1], q_dtype, kv_dtype,
-                     out_dtype, scale, num_splits)
-    rows = H * G if variant == "mlra" else H
-    odt = torch.float32 if out_dtype == "f32" else torch.bfloat16
-    dev = q_latent.device
-    if out is None:
-        out = torch.empty((B, H, G, d) if variant == "mlra" else (B, H, d), dtype=odt, device=dev)
-    if lse is None:
-        lse = torch.empty((B, H, G) if variant == "mlra" else (B, H), dtype=torch.float32, device=dev)
-    _need(out, "out", (odt,))
-    _need(lse, "lse", (torch.float32,))
-    if out.numel() != B * rows * d or lse.numel() != B * rows:
-        raise ValueError("out/lse have the wrong size")
-    ws_bytes = workspace_size(p)
-    if workspace is None:
-        workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
-    _need(workspace, "workspace")
-    cache = KVCache(k.data_ptr(), None if rope is None else rope.data_ptr(),
-                    None if v is None else v.data_ptr(), None if kscale is None else kscale.data_ptr())
-    if stream is None:
-        stream = torch.cuda.current_stream(dev).cuda_stream
-    st = lib().ld_latent_decode(ctypes.byref(p), _ptr(q_latent), _ptr(q_rope), ctypes.byref(cache),
-                                _ptr(block_table), _ptr(seq_lens), _ptr(out), _ptr(lse), _ptr(workspace),
-                                workspace.numel() * workspace.element_size(), ctypes.c_void_p(stream))
-    if st:
-        raise LatentDecodeError(st, "ld_latent_decode")
-    return out, lse
+    """One decode step; returns (out, lse).  See ``Decoder`` for the arguments."""
+    d = Decoder(q_latent, q_rope, k, block_table, seq_lens, variant=variant, scale=scale, groups=groups, v=v,
+                rope=rope, kscale=kscale, out=out, lse=lse, out_dtype=out_dtype, num_splits=num_splits,
+                workspace=workspace)
+    return d.run(stream)
 
 
 def split_kv_combine(partial_out, partial_lse, row_num_splits, *, out_dtype: str = "f32", out=None, lse=None,

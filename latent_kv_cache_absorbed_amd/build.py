@@ -24,6 +24,8 @@ SOURCES = ["api.cpp", "plan_combine.hip", "decode.hip"]
 COMMON = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-I", INCLUDE, "-I", CSRC,
           # packed fp32 VALU forms are kept out of every kernel
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          # keep MFMA accumulators in the unified VGPR file (avoids AGPR round trips and spills)
+          "-mllvm", "-amdgpu-mfma-vgpr-form=1",
           "-Wall", "-Wno-unused-function"]
 
 

@@ -219,58 +219,41 @@ int32_t ld_validate_metadata(const ld_problem* p, const int32_t* block_table_hos
   return LD_OK;
 }
 
-int32_t ld_latent_decode(const ld_problem* p, const void* q_latent, const void* q_rope, const ld_kv_cache* cache,
-                         const int32_t* block_table, const int32_t* seq_lens, void* out, float* lse, void* workspace,
-                         size_t workspace_bytes, void* stream) {
-  const int32_t st = ld_check_problem(p);
-  if (st != LD_OK) return st;
-  if (p->batch == 0) return LD_OK;
+}  // extern "C"
+
+namespace {
+
+int32_t check_pointers(const ld_problem* p, const void* q_latent, const void* q_rope, const ld_kv_cache* cache,
+                       const int32_t* block_table, const int32_t* seq_lens, const void* out, const float* lse) {
   const bool lat = latent(*p);
   const bool fp8 = p->kv_dtype == LD_FP8_E4M3;
-  if (!q_latent || !cache || !cache->k || !block_table || !seq_lens || !out || !lse || !workspace)
-    return LD_ERR_NULL_POINTER;
+  if (!q_latent || !cache || !cache->k || !block_table || !seq_lens || !out || !lse) return LD_ERR_NULL_POINTER;
   if (lat && !q_rope) return LD_ERR_NULL_POINTER;
   if (fp8 && (!cache->rope || !cache->scale)) return LD_ERR_NULL_POINTER;
   if ((p->variant == LD_VARIANT_GQA || p->variant == LD_VARIANT_MQA) && !cache->v) return LD_ERR_NULL_POINTER;
   if (!aligned(q_latent, 16) || (lat && !aligned(q_rope, 16)) || !aligned(cache->k, 16) || !aligned(out, 16) ||
-      !aligned(lse, 4) || !aligned(block_table, 4) || !aligned(seq_lens, 4) || !aligned(workspace, 256))
+      !aligned(lse, 4) || !aligned(block_table, 4) || !aligned(seq_lens, 4))
     return LD_ERR_MISALIGNED;
   if (cache->v && !aligned(cache->v, 16)) return LD_ERR_MISALIGNED;
   if (fp8 && (!aligned(cache->rope, 16) || !aligned(cache->scale, 4))) return LD_ERR_MISALIGNED;
+  return LD_OK;
+}
 
-  const int cus = device_cu_count();
-  const WsLayout w = ws_layout(*p, cus);
-  if (workspace_bytes < w.total) return LD_ERR_WORKSPACE_TOO_SMALL;
+int32_t check_workspace(const ld_problem* p, const void* workspace, size_t workspace_bytes, WsLayout* w) {
+  if (!workspace) return LD_ERR_NULL_POINTER;
+  if (!aligned(workspace, 256)) return LD_ERR_MISALIGNED;
+  *w = ws_layout(*p, device_cu_count());
+  if (workspace_bytes < w->total) return LD_ERR_WORKSPACE_TOO_SMALL;
+  return LD_OK;
+}
+
+DecodeArgs decode_args(const ld_problem* p, const WsLayout& w, void* workspace) {
   const Shape s = launch_shape(*p);
   char* ws = static_cast<char*>(workspace);
-
-  PlanArgs pa;
-  pa.seq_lens = seq_lens;
-  pa.header = reinterpret_cast<int32_t*>(ws + w.header);
-  pa.units = reinterpret_cast<Unit*>(ws + w.units);
-  pa.seqs = reinterpret_cast<int32_t*>(ws + w.seqs);
-  pa.batch = p->batch;
-  pa.capacity = p->max_pages_per_seq * p->page_size;
-  pa.page_size = p->page_size;
-  pa.target_units = target_units_for(*p, cus);
-  pa.forced_splits = p->num_splits;
-  pa.max_units = w.max_units;
-  if (launch_plan(pa, stream) != hipSuccess) return LD_ERR_HIP;
-
-  DecodeArgs a;
-  a.q_lat = q_latent;
-  a.q_rope = q_rope;
-  a.k = cache->k;
-  a.rope = cache->rope;
-  a.v = cache->v;
-  a.kscale = cache->scale;
-  a.block_table = block_table;
-  a.seq_lens = seq_lens;
-  a.out = out;
-  a.lse = lse;
-  a.header = pa.header;
-  a.units = pa.units;
-  a.seqs = pa.seqs;
+  DecodeArgs a{};
+  a.header = reinterpret_cast<const int32_t*>(ws + w.header);
+  a.units = reinterpret_cast<const Unit*>(ws + w.units);
+  a.seqs = reinterpret_cast<const int32_t*>(ws + w.seqs);
   a.part_lse = reinterpret_cast<float*>(ws + w.part_lse);
   a.part_out = reinterpret_cast<float*>(ws + w.part_out);
   a.batch = p->batch;
@@ -288,11 +271,97 @@ int32_t ld_latent_decode(const ld_problem* p, const void* q_latent, const void* 
   a.out_bf16 = p->out_dtype == LD_BF16;
   a.mlra = p->variant == LD_VARIANT_MLRA;
   a.scale_log2 = p->softmax_scale * 1.4426950408889634f;
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t ld_plan(const ld_problem* p, const int32_t* seq_lens, void* workspace, size_t workspace_bytes, void* stream) {
+  const int32_t st = ld_check_problem(p);
+  if (st != LD_OK) return st;
+  if (p->batch == 0) return LD_OK;
+  if (!seq_lens) return LD_ERR_NULL_POINTER;
+  if (!aligned(seq_lens, 4)) return LD_ERR_MISALIGNED;
+  WsLayout w;
+  const int32_t sw = check_workspace(p, workspace, workspace_bytes, &w);
+  if (sw != LD_OK) return sw;
+  char* ws = static_cast<char*>(workspace);
+  PlanArgs pa;
+  pa.seq_lens = seq_lens;
+  pa.header = reinterpret_cast<int32_t*>(ws + w.header);
+  pa.units = reinterpret_cast<Unit*>(ws + w.units);
+  pa.seqs = reinterpret_cast<int32_t*>(ws + w.seqs);
+  pa.batch = p->batch;
+  pa.capacity = p->max_pages_per_seq * p->page_size;
+  pa.page_size = p->page_size;
+  pa.target_units = target_units_for(*p, device_cu_count());
+  pa.forced_splits = p->num_splits;
+  pa.max_units = w.max_units;
+  return launch_plan(pa, stream) == hipSuccess ? LD_OK : LD_ERR_HIP;
+}
+
+int32_t ld_decode_planned(const ld_problem* p, const void* q_latent, const void* q_rope, const ld_kv_cache* cache,
+                          const int32_t* block_table, const int32_t* seq_lens, void* out, float* lse,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  const int32_t st = ld_check_problem(p);
+  if (st != LD_OK) return st;
+  if (p->batch == 0) return LD_OK;
+  const int32_t sp = check_pointers(p, q_latent, q_rope, cache, block_table, seq_lens, out, lse);
+  if (sp != LD_OK) return sp;
+  WsLayout w;
+  const int32_t sw = check_workspace(p, workspace, workspace_bytes, &w);
+  if (sw != LD_OK) return sw;
+  DecodeArgs a = decode_args(p, w, workspace);
+  a.q_lat = q_latent;
+  a.q_rope = q_rope;
+  a.k = cache->k;
+  a.rope = cache->rope;
+  a.v = cache->v;
+  a.kscale = cache->scale;
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  a.out = out;
+  a.lse = lse;
   const int r = launch_decode(*p, a, stream);
   if (r == -1) return LD_ERR_UNSUPPORTED;
-  if (r != hipSuccess) return LD_ERR_HIP;
-  if (launch_combine_ws(a, p->d_latent, stream) != hipSuccess) return LD_ERR_HIP;
-  return LD_OK;
+  return r == hipSuccess ? LD_OK : LD_ERR_HIP;
+}
+
+int32_t ld_combine_planned(const ld_problem* p, void* out, float* lse, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  const int32_t st = ld_check_problem(p);
+  if (st != LD_OK) return st;
+  if (p->batch == 0) return LD_OK;
+  if (!out || !lse) return LD_ERR_NULL_POINTER;
+  if (!aligned(out, 16) || !aligned(lse, 4)) return LD_ERR_MISALIGNED;
+  WsLayout w;
+  const int32_t sw = check_workspace(p, workspace, workspace_bytes, &w);
+  if (sw != LD_OK) return sw;
+  DecodeArgs a = decode_args(p, w, workspace);
+  a.out = out;
+  a.lse = lse;
+  return launch_combine_ws(a, p->d_latent, stream) == hipSuccess ? LD_OK : LD_ERR_HIP;
+}
+
+int32_t ld_latent_decode(const ld_problem* p, const void* q_latent, const void* q_rope, const ld_kv_cache* cache,
+                         const int32_t* block_table, const int32_t* seq_lens, void* out, float* lse, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  const int32_t st = ld_check_problem(p);
+  if (st != LD_OK) return st;
+  if (p->batch == 0) return LD_OK;
+  const int32_t sp = check_pointers(p, q_latent, q_rope, cache, block_table, seq_lens, out, lse);
+  if (sp != LD_OK) return sp;
+  WsLayout w;
+  const int32_t sw = check_workspace(p, workspace, workspace_bytes, &w);
+  if (sw != LD_OK) return sw;
+  int32_t r = ld_plan(p, seq_lens, workspace, workspace_bytes, stream);
+  if (r != LD_OK) return r;
+  r = ld_decode_planned(p, q_latent, q_rope, cache, block_table, seq_lens, out, lse, workspace, workspace_bytes,
+                        stream);
+  if (r != LD_OK) return r;
+  return ld_combine_planned(p, out, lse, workspace, workspace_bytes, stream);
 }
 
 int32_t ld_split_kv_combine(int32_t num_rows, int32_t d_v, int32_t max_splits, const float* partial_out,

@@ -23,7 +23,16 @@ namespace ld {
 namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
+
+// ds_read_b64_tr_b16: within each group of 16 lanes, lane i receives element i%4 of the
+// 8-byte loads of lanes 4k + i/4, k = 0..3 (so four lanes that load four consecutive
+// elements of four rows hand every lane one column of those rows).
+__device__ __forceinline__ bf16x4_t lds_read_tr(const char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(p));
+}
 
 enum KvT : int { KV_F32 = 0, KV_BF16 = 1, KV_FP8 = 2 };
 
@@ -84,20 +93,17 @@ __device__ __forceinline__ int lds_byte(int t, int row_bytes, int byte_in_row, i
   return t * row_bytes + (((c ^ (t & swm)) << 4) | (byte_in_row & 15));
 }
 
-// fp8 E4M3 (OCP) -> bf16, exact: 8 codes in, 8 bf16 out.
+// fp8 E4M3 (OCP) -> bf16, exact: 8 codes in, 8 bf16 out.  v_cvt_scalef32_pk_bf16_fp8 with
+// scale 1 converts two codes straight to two bf16 (every E4M3 value is a bf16 value).  (Going
+// through v_cvt_pk_f32_fp8 and repacking the f32 halves was mis-combined by the compiler into
+// a copy of one half, so the direct conversion is used.)
 __device__ __forceinline__ uint4 e4m3x8_to_bf16x8(uint2 codes) {
-  uint4 r;
-  unsigned* o = reinterpret_cast<unsigned*>(&r);
-  const unsigned w[2] = {codes.x, codes.y};
-#pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    // two codes -> two f32 per conversion; the f32 -> bf16 truncation is exact (<= 4 significant bits)
-    const auto f0 = __builtin_amdgcn_cvt_pk_f32_fp8(w[k], false);
-    const auto f1 = __builtin_amdgcn_cvt_pk_f32_fp8(w[k], true);
-    o[2 * k] = (__builtin_bit_cast(unsigned, f0[0]) >> 16) | (__builtin_bit_cast(unsigned, f0[1]) & 0xFFFF0000u);
-    o[2 * k + 1] = (__builtin_bit_cast(unsigned, f1[0]) >> 16) | (__builtin_bit_cast(unsigned, f1[1]) & 0xFFFF0000u);
-  }
-  return r;
+  const auto a0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes.x, 1.0f, false);
+  const auto a1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes.x, 1.0f, true);
+  const auto b0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes.y, 1.0f, false);
+  const auto b1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes.y, 1.0f, true);
+  return make_uint4(__builtin_bit_cast(unsigned, a0), __builtin_bit_cast(unsigned, a1),
+                    __builtin_bit_cast(unsigned, b0), __builtin_bit_cast(unsigned, b1));
 }
 
 template <int KV, int DL, int DR, int KIND>
@@ -277,18 +283,23 @@ __global__ __launch_bounds__(MAXT) void decode_kernel(DecodeArgs a) {
   // Per-lane LDS byte offsets (bf16 path).  S operand: the 16-byte chunk (2ks + h) of row tr,
   // swizzled; its low three chunk bits depend on ks only through ks & 3.
   int kbase[4];
-  int vbase[2][8];
+  int vbase[2][2];
   if constexpr (M::EPL == 8) {
     const int key = tr & SWM_K;
 #pragma unroll
     for (int q = 0; q < 4; ++q) kbase[q] = tr * KW + 16 * (((2 * q + h) & SWM_K) ^ key) + 16 * ((2 * q + h) & ~SWM_K);
-    // V^T operand: element (token 16ps + 8h + j, column s*DL + 32cb + col); the swizzle key is j
+    // V^T operand via transposed reads.  Lane group g = lane/16 serves columns 16*(g%2) + (lane%16)
+    // of a 32-column block and tokens 8*(g/2) + 4*rb + [0, 4) of a 16-token k-step; its source
+    // lane L = lane%16 loads columns 4*(L%4) .. +3 of token 8*(g/2) + 4*rb + L/4.
+    const int g16 = lane >> 4;
+    const int L16 = lane & 15;
 #pragma unroll
     for (int c1 = 0; c1 < 2; ++c1)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int chunk = 4 * c1 + (col >> 3);
-        vbase[c1][j] = 8 * h * VROW + 2 * (col & 7) + 16 * (((chunk & SWM_VR) ^ (j & SWM_VR)) + (chunk & ~SWM_VR));
+      for (int rb = 0; rb < 2; ++rb) {
+        const int tt = 8 * (g16 >> 1) + 4 * rb + (L16 >> 2);
+        const int chunk = 4 * c1 + 2 * (g16 & 1) + ((L16 & 3) >> 1);
+        vbase[c1][rb] = tt * VROW + 16 * (((chunk & SWM_VR) ^ (tt & SWM_VR)) + (chunk & ~SWM_VR)) + 8 * (L16 & 1);
       }
   }
 
@@ -380,14 +391,10 @@ __global__ __launch_bounds__(MAXT) void decode_kernel(DecodeArgs a) {
       for (int p2 = 0; p2 < M::PSTEPS; ++p2) {
         Frag af;
         if constexpr (M::EPL == 8) {
-          bf16x8_t f;
-          const int cstat = 16 * ((s * DL) / 8 + ((4 * cb) & ~7));
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const char* p = vsrc + vbase[cb & 1][j] + (16 * p2 + j) * VROW + cstat;
-            f[j] = *reinterpret_cast<const __bf16*>(p);
-          }
-          af = f;
+          const int cstat = 16 * p2 * VROW + 16 * ((s * DL) / 8 + ((4 * cb) & ~7));
+          const bf16x4_t lo = lds_read_tr(vsrc + vbase[cb & 1][0] + cstat);
+          const bf16x4_t hi = lds_read_tr(vsrc + vbase[cb & 1][1] + cstat);
+          af = bf16x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         } else {
           const int tt = 2 * p2 + h;
           af = *reinterpret_cast<const float*>(vsrc + lds_byte(tt, VROW, (s * DL + cb * 32 + col) * ES, SWM_VR));
