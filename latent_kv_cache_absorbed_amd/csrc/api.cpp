@@ -15,27 +15,20 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
 bool latent(const ld_problem& p) { return p.variant <= LD_VARIANT_MLRA; }
 
-int elem_bytes_lds(int kv) { return kv == LD_F32 ? 4 : 2; }  // fp8 is staged as bf16
-
 struct Shape {
   int heads_per_set = 0, hblocks = 0, nsets = 0, wg_per_unit = 0;
 };
 
-// Sets per work group: the largest of 8, 4, 2, 1 that divides G and whose waves and LDS
-// tile fit the kernel built for this shape.
+// Sets per work group: the largest of 8, 4, 2, 1 that divides G and has a kernel built for it
+// (with one wave per 32 heads of each set).
 Shape launch_shape(const ld_problem& p) {
   Shape s;
   const int H = p.num_q_heads, G = p.num_groups;
   s.heads_per_set = p.variant == LD_VARIANT_MLRA ? H : H / G;
   s.hblocks = (s.heads_per_set + 31) / 32;
-  const int es = elem_bytes_lds(p.kv_dtype);
   for (int n = 8; n >= 1; n >>= 1) {
-    if (n > kernel_max_sets(p) || G % n) continue;
-    if (n * s.hblocks * kWaveSize > kernel_max_threads(p)) continue;
-    size_t lds = (size_t)kTile * ((size_t)(n * p.d_latent + p.d_rope) * es);
-    if (p.variant == LD_VARIANT_GQA || p.variant == LD_VARIANT_MQA) lds += (size_t)kTile * n * p.d_latent * es;
-    if (p.kv_dtype == LD_FP8_E4M3) lds += kTile * sizeof(float);
-    if (lds > 160 * 1024) continue;
+    if (G % n) continue;
+    if (!decode_instantiated(p, n, n * s.hblocks)) continue;
     s.nsets = n;
     s.wg_per_unit = G / n;
     break;
@@ -150,7 +143,8 @@ int32_t ld_check_problem(const ld_problem* p) {
   } else {
     return LD_ERR_BAD_DTYPE;
   }
-  if (!decode_supported(*p)) return LD_ERR_UNSUPPORTED;
+  // stages of 32 tokens must not straddle pages
+  if (p->page_size % kTile) return LD_ERR_UNSUPPORTED;
   if (launch_shape(*p).nsets == 0) return LD_ERR_UNSUPPORTED;
   return LD_OK;
 }
