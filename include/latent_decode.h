@@ -117,7 +117,8 @@ typedef struct ld_problem {
   int32_t q_dtype;           /* ld_dtype of q_latent and q_rope: F32 or BF16 */
   int32_t kv_dtype;          /* ld_dtype of the cache: F32, BF16 or FP8_E4M3 (latent variants) */
   int32_t out_dtype;         /* ld_dtype of out: F32 or BF16 */
-  float softmax_scale;       /* multiplies q.k; lse is reported in this scaled domain */
+  float softmax_scale;       /* multiplies q.k; positive and finite (else LD_ERR_BAD_SHAPE);
+                                lse is reported in this scaled domain */
   int32_t num_splits;        /* 0: the planner splits long sequences over CUs; n >= 1: at most n splits */
 } ld_problem;
 

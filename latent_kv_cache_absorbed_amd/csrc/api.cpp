@@ -20,7 +20,7 @@ struct Shape {
 };
 
 // Sets per work group: the largest of 8, 4, 2, 1 that divides G and has a kernel built for it
-// (with one wave per 32 heads of each set).
+// (covering all of a set's heads in blocks of 32).
 Shape launch_shape(const ld_problem& p) {
   Shape s;
   const int H = p.num_q_heads, G = p.num_groups;
@@ -28,7 +28,7 @@ Shape launch_shape(const ld_problem& p) {
   s.hblocks = (s.heads_per_set + 31) / 32;
   for (int n = 8; n >= 1; n >>= 1) {
     if (G % n) continue;
-    if (!decode_instantiated(p, n, n * s.hblocks)) continue;
+    if (!decode_instantiated(p, n, s.hblocks)) continue;
     s.nsets = n;
     s.wg_per_unit = G / n;
     break;
@@ -112,7 +112,7 @@ int32_t ld_check_problem(const ld_problem* p) {
     return LD_ERR_BAD_SHAPE;
   if ((long long)p->max_pages_per_seq * p->page_size > 0x7fffffffLL) return LD_ERR_BAD_SHAPE;
   if (p->num_splits < 0) return LD_ERR_BAD_SHAPE;
-  if (!std::isfinite(p->softmax_scale)) return LD_ERR_BAD_SHAPE;
+  if (!std::isfinite(p->softmax_scale) || !(p->softmax_scale > 0.f)) return LD_ERR_BAD_SHAPE;
   const int H = p->num_q_heads, G = p->num_groups;
   switch (p->variant) {
     case LD_VARIANT_MLA:

@@ -4,16 +4,23 @@
 // Work decomposition.  A work unit is (sequence b, token chunk [t_begin, t_end)) from the
 // split-KV planner.  A "set" is a group of query heads that score against the same cached
 // rows: all H heads for MLA, one latent group for GLA, one branch for MLRA, one kv head for
-// GQA/GTA, all heads for MQA.  A work group handles NSETS sets of one unit; each of its
-// WAVES waves owns one set and 32 of that set's heads.  Per 32-token stage the work group
-// copies the rows it needs into LDS once (asynchronous global->LDS DMA, double-buffered, so
-// stage n+1 streams in while stage n is computed), and every wave reads them from there:
+// GQA/GTA, all heads for MQA.  A work group handles NSETS sets of one unit, HB blocks of 32
+// heads per set and SPLIT waves per head block.  Per 32-token stage the work group copies the
+// rows it needs into LDS once (asynchronous global->LDS DMA into one of NBUF stage buffers, so
+// later stages stream in while one is computed), and every wave reads them from there:
 //
 //   S^T[token, head] = K_stage . Q^T           (v_mfma_f32_32x32x16_bf16; Q stays in VGPRs)
 //   online softmax over the token axis         (each lane owns one head: 16 scores here and
 //                                               16 in the lane 32 apart)
 //   O^T[col, head]  += V_stage^T . P^T          (same MFMA; P never leaves registers; the V^T
 //                                               operand comes from ds_read_b64_tr_b16)
+//
+// With SPLIT = 2 the two waves of a head block share its work: each scores over half of the
+// latent dims and half of the rope dims, the pair adds its two partial scores through LDS
+// (floating-point addition commutes, so both waves hold bit-identical scores and run the same
+// softmax), and each wave then accumulates half of the V columns.  A wave so holds half the
+// query and accumulator registers (for MLA 72 + 128 instead of 144 + 256), two waves fit on a
+// SIMD, and each hides the other's LDS latency.
 //
 // The rows of the S MFMA are a fixed permutation of the stage's tokens, chosen so that the
 // score layout the MFMA writes is exactly the P^T operand layout the PV MFMA reads.
@@ -34,6 +41,7 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
 
 enum KvT : int { KV_F32 = 0, KV_BF16 = 1, KV_FP8 = 2 };
@@ -49,6 +57,20 @@ constexpr float kRescaleSlack = 8.f;
 __device__ __forceinline__ bf16x4_t lds_read_tr(const char* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(p));
 }
+
+// s_waitcnt vmcnt(N) (gfx9 encoding: vmcnt bits [3:0] and [15:14]; expcnt and lgkmcnt left at
+// their no-wait maxima).  Counts above the 6-bit field's 63 wait for 63 instead (a stricter wait).
+template <int N0>
+__device__ __forceinline__ void wait_vmcnt() {
+  constexpr int N = N0 > 63 ? 63 : N0;
+  static_assert(N >= 0, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Work-group barrier that orders LDS only.  __syncthreads() also fences global memory, which
+// makes every wave drain all in-flight global->LDS copies (vmcnt 0) and defeats the stage
+// pipeline; here the caller waits for exactly the copies it needs (wait_vmcnt) first.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // 16-byte global -> LDS copy per lane; the LDS destination of lane i is lds + 16 i.
 __device__ __forceinline__ void dma16(const void* gsrc, char* lds_wave_base) {
@@ -100,16 +122,22 @@ __device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? l
 
 constexpr int ilog2(int x) { return x <= 1 ? 0 : 1 + ilog2(x / 2); }
 constexpr bool pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+constexpr int cmin(int a, int b) { return a < b ? a : b; }
 
-// Chunk swizzle of an LDS row of `rb` bytes: the low bits of the 16-byte chunk index are XORed
-// with key(t) = 2*(t%4) + bit 3 of t.  The 8 storage rows one S-operand read serves per cycle
-// ({0,1,2,3,8,9,10,11} + 4j, see row_token) get 8 distinct keys, and the 4 consecutive rows a
-// transposed V read touches get keys that differ above bit 0, so neither read pattern has bank
-// conflicts.
-__host__ __device__ constexpr int swz_mask(int rb) { return rb >= 128 ? 7 : rb >= 64 ? 3 : rb >= 32 ? 1 : 0; }
-__device__ __forceinline__ int swz_key(int t) { return ((t & 3) << 1) | ((t >> 3) & 1); }
-__device__ __forceinline__ int lds_off(int t, int rb, int byte_in_row) {
-  const int m = swz_mask(rb);
+// Chunk swizzle of an LDS row: the low bits (mask m, at most four bits) of the 16-byte chunk
+// index are XORed with a key of the row's token t, key bits = (t2^t3, t0, t1, t3^t0).  The key
+// is a bijection on every 16 consecutive rows, and its bits 2 and 3 take four distinct values on
+// every 4 consecutive rows.  So neither the S-operand reads (16 lanes of a cycle cover 16
+// distinct rows mod 16, one chunk each) nor the transposed V reads (4 consecutive rows x 4
+// chunks per 16 lanes) hit a bank twice, whether the LDS serves 16 lanes a cycle over 64 banks
+// or 8 lanes over 32 banks.
+__host__ __device__ constexpr int swz_mask(int rb) {
+  return rb >= 256 ? 15 : rb >= 128 ? 7 : rb >= 64 ? 3 : rb >= 32 ? 1 : 0;
+}
+__device__ __forceinline__ int swz_key(int t) {
+  return (((t >> 2) ^ (t >> 3)) & 1) | ((t & 1) << 1) | (((t >> 1) & 1) << 2) | ((((t >> 3) ^ t) & 1) << 3);
+}
+__device__ __forceinline__ int lds_off(int t, int rb, int m, int byte_in_row) {
   const int c = byte_in_row >> 4;
   return t * rb + ((((c & m) ^ (swz_key(t) & m)) | (c & ~m)) << 4) + (byte_in_row & 15);
 }
@@ -130,66 +158,101 @@ __device__ __forceinline__ uint4 e4m3x8_to_bf16x8(unsigned lo, unsigned hi) {
 // ------------------------------------------------------------------------------------------
 // compile-time shape of one kernel instance
 // ------------------------------------------------------------------------------------------
-template <int KV, int DL, int DR, int KIND, int NSETS, int WAVES>
+template <int KV, int DL, int DR, int KIND, int NSETS, int HB, int SPLIT>
 struct Cfg {
   using M = Mma<KV>;
   using CT = typename M::CT;
   static constexpr int ES = sizeof(CT);                       // LDS element bytes (fp8 staged as bf16)
   static constexpr int GES = (KV == KV_FP8) ? 1 : ES;         // global latent element bytes
+  static constexpr int WAVES = NSETS * HB * SPLIT;
   static constexpr int THREADS = WAVES * kWaveSize;
-  static constexpr int DK = DL + DR;                          // score dims per set
-  static constexpr int KS = DK / M::KSTEP;                    // k-steps of S
+  static constexpr int KL = DL / M::KSTEP;                    // latent (K) k-steps of S
+  static constexpr int KR = DR / M::KSTEP;                    // rope k-steps of S
+  static constexpr int KLW = KL / SPLIT, KRW = KR / SPLIT;    // k-steps per wave
   static constexpr int CB = DL / 32;                          // 32-column blocks of O
+  static constexpr int CBW = CB / SPLIT;                      // column blocks per wave
   static constexpr int LW = NSETS * DL * ES;                  // latent / K row bytes in LDS
   static constexpr int RW = DR * ES;                          // rope row bytes in LDS
   static constexpr int VW = (KIND == KIND_SHARED) ? NSETS * DL * ES : 0;
+  // swizzle masks; a set's slice of a row starts on a swizzle-group boundary
+  static constexpr int SETCH = DL * ES / 16;                  // chunks per set slice
+  static constexpr int MLS = cmin(SETCH - 1, swz_mask(LW));
+  static constexpr int MR = swz_mask(RW > 0 ? RW : 32);
+  static constexpr int MV = (KIND == KIND_SHARED) ? cmin(SETCH - 1, swz_mask(VW > 0 ? VW : 32)) : MLS;
   static constexpr int LAT_OFF = 0;
   static constexpr int ROPE_OFF = kTile * LW;
   static constexpr int V_OFF = ROPE_OFF + kTile * RW;
   static constexpr int SC_OFF = V_OFF + kTile * VW;
   static constexpr int BUF = SC_OFF + ((KV == KV_FP8) ? kTile * 4 : 0);
   static constexpr int BUF_AL = (BUF + 127) / 128 * 128;
-  static constexpr int LDS_BYTES = 2 * BUF_AL;
+  static constexpr int EXCH = (SPLIT == 2) ? WAVES * 16 * 64 * 4 : 16;   // partial-score exchange
+  // stage buffers: as many as fit (up to 4); the fp8 path stages through registers and keeps two
+  static constexpr int NB_FIT = (160 * 1024 - EXCH) / BUF_AL;
+  static constexpr int NBUF = (KV == KV_FP8) ? 2 : cmin(NB_FIT, 4);
+  static constexpr int LDS_TOTAL = 2 * BUF_AL + (NBUF > 2 ? BUF_AL : 128) + (NBUF > 3 ? BUF_AL : 128) + EXCH;
   static constexpr int VRB = (KIND == KIND_SHARED) ? VW : LW;   // row bytes of the V source region
   static constexpr int V_REG = (KIND == KIND_SHARED) ? V_OFF : LAT_OFF;
   static constexpr int FP8_ITEMS = kTile * NSETS * DL / 16;      // 16-code pieces of an fp8 stage
   static constexpr int FP8_PER_THREAD = (KV == KV_FP8) ? (FP8_ITEMS + THREADS - 1) / THREADS : 1;
-  static_assert(DK % M::KSTEP == 0 && DL % 32 == 0, "unsupported dims");
+  // 1 KB DMA blocks per stage (all regions) and the fewest any wave issues per stage
+  static constexpr int DMA_BLOCKS = (KV == KV_FP8) ? kTile * RW / 1024 : kTile * (LW + RW + VW) / 1024;
+  static constexpr int DMA_MIN_PER_WAVE = DMA_BLOCKS / WAVES;
+  static_assert(DL % 32 == 0 && DL % M::KSTEP == 0 && DR % M::KSTEP == 0, "unsupported dims");
+  static_assert(KL % SPLIT == 0 && KR % SPLIT == 0 && CB % SPLIT == 0, "dims must split evenly");
+  static_assert(SPLIT == 1 || M::EPL == 8, "split waves need the bf16 operand path");
+  // a wave's latent k-steps and column blocks must start on swizzle-group boundaries
+  static_assert(SPLIT == 1 || ((2 * KLW) % (MLS + 1) == 0 && (4 * CBW) % (MV + 1) == 0), "split alignment");
+  static_assert(SETCH % (MLS + 1) == 0, "set alignment");
   static_assert(pow2(LW) && LW >= 32 && (DR == 0 || (pow2(RW) && RW >= 32)), "row sizes must be powers of two");
   static_assert((kTile * LW) % 1024 == 0 && (kTile * RW) % 1024 == 0, "regions must be whole DMA blocks");
-  static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+  static_assert(NBUF >= 2 && LDS_TOTAL <= 160 * 1024, "LDS budget");
 };
 
-// One region of a stage: kTile rows of RB bytes, filled by 1 KB DMA blocks.  Block q (of
-// kTile*RB/1024) covers region bytes [1024q, 1024q + 1024); lane i lands at byte 1024q + 16i.
-// `src_row(t)` is the global address of stage token t's row, `src_col(byte)` the byte offset in
-// that row of a logical LDS row byte.
-template <int RB, class RowFn, class ColFn>
-__device__ __forceinline__ void dma_region(char* region, int wave, int nwaves, int lane, RowFn src_row,
-                                           ColFn src_col) {
+// One region of a stage: kTile rows of RB bytes (swizzle mask MSK), filled by 1 KB DMA blocks.
+// Block q covers region bytes [1024q, 1024q + 1024); lane i lands at byte 1024q + 16i.  Blocks
+// are dealt to the NW waves round-robin across all regions of a stage (FIRST is this region's
+// first block in that order), so every wave issues the floor or the ceiling of blocks / NW.
+// `src_row(t)` is the global address of stage token t's row, `src_col(b)` the byte offset in
+// that row of logical LDS row byte b.
+template <int RB, int MSK, int NW, int FIRST, class RowFn, class ColFn>
+__device__ __forceinline__ void dma_region(char* region, int wave, int lane, RowFn src_row, ColFn src_col) {
   constexpr int blocks = kTile * RB / 1024;
-  constexpr int m = swz_mask(RB);
-  for (int q = wave; q < blocks; q += nwaves) {
-    const int o = q * 1024 + lane * 16;
-    const int t = o >> ilog2(RB);
-    const int cp = (o & (RB - 1)) >> 4;                       // physical chunk in the row
-    const int c = (cp & ~m) | ((cp & m) ^ (swz_key(t) & m));  // logical chunk it must hold
-    dma16(src_row(t) + src_col(c << 4), region + q * 1024);
+  constexpr int iters = (blocks + NW - 1) / NW;
+  constexpr int shift = FIRST % NW;
+  const int q0 = wave >= shift ? wave - shift : wave - shift + NW;
+#pragma unroll
+  for (int i = 0; i < iters; ++i) {
+    const int q = q0 + i * NW;
+    if (blocks % NW == 0 || q < blocks) {
+      const int o = q * 1024 + lane * 16;
+      const int t = o >> ilog2(RB);
+      const int cp = (o & (RB - 1)) >> 4;                             // physical chunk in the row
+      const int c = (cp & ~MSK) | ((cp & MSK) ^ (swz_key(t) & MSK));  // logical chunk it must hold
+      dma16(src_row(t) + src_col(c << 4), region + q * 1024);
+    }
   }
 }
 
 // ------------------------------------------------------------------------------------------
 // the decode kernel
 // ------------------------------------------------------------------------------------------
-template <int KV, int DL, int DR, int KIND, int NSETS, int WAVES>
-__global__ __launch_bounds__(WAVES * 64) void decode_kernel(DecodeArgs a) {
-  using C = Cfg<KV, DL, DR, KIND, NSETS, WAVES>;
+template <int KV, int DL, int DR, int KIND, int NSETS, int HB, int SPLIT>
+__global__ __launch_bounds__(NSETS* HB* SPLIT * 64) void decode_kernel(DecodeArgs a,
+                                                                       const int32_t* __restrict__ block_table) {
+  using C = Cfg<KV, DL, DR, KIND, NSETS, HB, SPLIT>;
   using M = typename C::M;
   using CT = typename C::CT;
   using Frag = typename M::Frag;
   constexpr int ES = C::ES;
-  constexpr int HB = WAVES / NSETS;  // 32-head blocks per set
-  extern __shared__ __attribute__((aligned(16))) char smem[];
+  constexpr int WAVES = C::WAVES;
+  // Stage buffers are separate LDS objects (and the stage loop is unrolled over them) so that
+  // the compiler's alias scopes tell the buffers apart: a read of stage n then waits only for
+  // the copies into stage n's buffer, not for every copy in flight.
+  __shared__ __attribute__((aligned(128))) char lds_b0[C::BUF_AL];
+  __shared__ __attribute__((aligned(128))) char lds_b1[C::BUF_AL];
+  __shared__ __attribute__((aligned(128))) char lds_b2[C::NBUF > 2 ? C::BUF_AL : 128];
+  __shared__ __attribute__((aligned(128))) char lds_b3[C::NBUF > 3 ? C::BUF_AL : 128];
+  __shared__ __attribute__((aligned(16))) float lds_exch[C::EXCH / 4];
 
   // XCD-aware mapping: all work groups of one unit land on the same XCD (ids = unit mod 8)
   const int x = blockIdx.x;
@@ -206,18 +269,19 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(DecodeArgs a) {
 
   const int set0 = sb * NSETS;
   const int G = a.groups;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform, kept in an SGPR
   const int lane = threadIdx.x & 63;
   const int h = lane >> 5;
   const int col = lane & 31;
-  const int s = wave / HB;          // wave-uniform
-  const int hb = wave - s * HB;
+  const int s = wave / (HB * SPLIT);  // wave-uniform: set, head block, half
+  const int hb = (wave / SPLIT) % HB;
+  const int half = wave % SPLIT;
   const int gs = set0 + s;
   const int head_in_set = hb * 32 + col;
   const bool valid = head_in_set < a.heads_per_set;
   const int head = (a.mlra ? 0 : gs * a.heads_per_set) + (valid ? head_in_set : 0);
   const int row = a.mlra ? head * G + gs : head;
-  const int32_t* bt_row = a.block_table + (size_t)b * a.max_pages;
+  const int32_t* __restrict__ bt_row = block_table + (size_t)b * a.max_pages;  // read with scalar loads
   const int page_size = a.page_size;
 
   // global row geometry (bytes): latent variants store [G latents | rope] per token (fp8: codes
@@ -232,14 +296,14 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(DecodeArgs a) {
     // every token of a stage lies in one page (stages are page aligned and page_size % 32 == 0)
     const int page = clampi(bt_row[stage0 / page_size], 0, a.num_pages - 1);
     const size_t r0 = (size_t)page * page_size + (stage0 % page_size);
-    const int tlast = t_end - 1 - stage0;                  // rows past the unit's end repeat its last row
+    const int tlast = t_end - 1 - stage0;  // rows past the unit's end repeat its last row
     if constexpr (KV != KV_FP8) {
-      dma_region<C::LW>(buf + C::LAT_OFF, wave, WAVES, lane,
-                        [&](int t) { return kbase + (r0 + min(t, tlast)) * (size_t)grow_bytes; },
-                        [&](int cb) {
-                          const int s2 = cb / (DL * ES);
-                          return (set0 + s2) * DL * ES + (cb - s2 * DL * ES);
-                        });
+      dma_region<C::LW, C::MLS, WAVES, 0>(buf + C::LAT_OFF, wave, lane,
+                                [&](int t) { return kbase + (r0 + min(t, tlast)) * (size_t)grow_bytes; },
+                                [&](int cb) {
+                                  const int s2 = cb / (DL * ES);
+                                  return (set0 + s2) * DL * ES + (cb - s2 * DL * ES);
+                                });
     } else {
       // codes -> registers now; converted and written after this stage's compute
 #pragma unroll
@@ -259,23 +323,23 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(DecodeArgs a) {
     if constexpr (KIND == KIND_LATENT && DR > 0) {
       if constexpr (KV == KV_FP8) {
         const char* rbase = static_cast<const char*>(a.rope);
-        dma_region<C::RW>(buf + C::ROPE_OFF, wave, WAVES, lane,
-                          [&](int t) { return rbase + (r0 + min(t, tlast)) * (size_t)(DR * 2); },
-                          [&](int cb) { return cb; });
+        dma_region<C::RW, C::MR, WAVES, 0>(buf + C::ROPE_OFF, wave, lane,
+                                 [&](int t) { return rbase + (r0 + min(t, tlast)) * (size_t)(DR * 2); },
+                                 [&](int cb) { return cb; });
       } else {
-        dma_region<C::RW>(buf + C::ROPE_OFF, wave, WAVES, lane,
-                          [&](int t) { return kbase + (r0 + min(t, tlast)) * (size_t)grow_bytes; },
-                          [&](int cb) { return G * DL * ES + cb; });
+        dma_region<C::RW, C::MR, WAVES, kTile * C::LW / 1024>(buf + C::ROPE_OFF, wave, lane,
+                                 [&](int t) { return kbase + (r0 + min(t, tlast)) * (size_t)grow_bytes; },
+                                 [&](int cb) { return G * DL * ES + cb; });
       }
     }
     if constexpr (KIND == KIND_SHARED) {
       const char* vbase_g = static_cast<const char*>(a.v);
-      dma_region<C::VW>(buf + C::V_OFF, wave, WAVES, lane,
-                        [&](int t) { return vbase_g + (r0 + min(t, tlast)) * (size_t)grow_bytes; },
-                        [&](int cb) {
-                          const int s2 = cb / (DL * ES);
-                          return (set0 + s2) * DL * ES + (cb - s2 * DL * ES);
-                        });
+      dma_region<C::VW, C::MV, WAVES, kTile *(C::LW + C::RW) / 1024>(buf + C::V_OFF, wave, lane,
+                               [&](int t) { return vbase_g + (r0 + min(t, tlast)) * (size_t)grow_bytes; },
+                               [&](int cb) {
+                                 const int s2 = cb / (DL * ES);
+                                 return (set0 + s2) * DL * ES + (cb - s2 * DL * ES);
+                               });
     }
   };
   // fp8: convert the prefetched codes and write them (and the scales) into buffer `buf`
@@ -288,8 +352,9 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(DecodeArgs a) {
           const int t = i / (NSETS * DL / 16);
           const int k16 = i - t * (NSETS * DL / 16);
           char* rowp = buf + C::LAT_OFF;
-          *reinterpret_cast<uint4*>(rowp + lds_off(t, C::LW, k16 * 32)) = e4m3x8_to_bf16x8(pre[r].x, pre[r].y);
-          *reinterpret_cast<uint4*>(rowp + lds_off(t, C::LW, k16 * 32 + 16)) = e4m3x8_to_bf16x8(pre[r].z, pre[r].w);
+          *reinterpret_cast<uint4*>(rowp + lds_off(t, C::LW, C::MLS, k16 * 32)) = e4m3x8_to_bf16x8(pre[r].x, pre[r].y);
+          *reinterpret_cast<uint4*>(rowp + lds_off(t, C::LW, C::MLS, k16 * 32 + 16)) =
+              e4m3x8_to_bf16x8(pre[r].z, pre[r].w);
         }
       }
       if (threadIdx.x < kTile) reinterpret_cast<float*>(buf + C::SC_OFF)[threadIdx.x] = pre_sc;
@@ -297,138 +362,201 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(DecodeArgs a) {
     (void)buf;
   };
 
-  // ---- this lane's query fragments (B operand of S^T = K . Q^T)
-  Frag qf[C::KS];
+  // ---- this lane's query fragments (B operand of S^T = K . Q^T) for the wave's k-steps:
+  // latent k-steps [half*KLW, +KLW) and rope k-steps [half*KRW, +KRW).  The loads are issued
+  // without branches (lanes past the set's heads read head 0 and are zeroed).
+  Frag ql[C::KLW];
+  Frag qr[C::KRW > 0 ? C::KRW : 1];
   {
     const size_t qrow = a.mlra ? ((size_t)b * a.heads + head) * G + gs : (size_t)b * a.heads + head;
+    const CT* qlp = static_cast<const CT*>(a.q_lat) + qrow * DL + half * C::KLW * M::KSTEP + h * M::EPL;
+    const CT* qrp = static_cast<const CT*>(a.q_rope) + qrow * DR + half * C::KRW * M::KSTEP + h * M::EPL;
+    if constexpr (M::EPL == 8) {
 #pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) {
-      const int d0 = ks * M::KSTEP + h * M::EPL;
-      const CT* src;
-      if (KIND != KIND_LATENT || ks * M::KSTEP < DL)
-        src = static_cast<const CT*>(a.q_lat) + qrow * DL + d0;
-      else
-        src = static_cast<const CT*>(a.q_rope) + qrow * DR + (d0 - DL);
-      if constexpr (M::EPL == 8) {
-        uint4 v = valid ? *reinterpret_cast<const uint4*>(src) : make_uint4(0u, 0u, 0u, 0u);
-        qf[ks] = __builtin_bit_cast(Frag, v);
-      } else {
-        qf[ks] = valid ? *src : 0.f;
+      for (int k = 0; k < C::KLW; ++k) {
+        uint4 v = *reinterpret_cast<const uint4*>(qlp + k * M::KSTEP);
+        if (!valid) v = make_uint4(0u, 0u, 0u, 0u);
+        ql[k] = __builtin_bit_cast(Frag, v);
+      }
+#pragma unroll
+      for (int j = 0; j < C::KRW; ++j) {
+        uint4 v = *reinterpret_cast<const uint4*>(qrp + j * M::KSTEP);
+        if (!valid) v = make_uint4(0u, 0u, 0u, 0u);
+        qr[j] = __builtin_bit_cast(Frag, v);
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < C::KLW; ++k) {
+        const float v = qlp[k * M::KSTEP];
+        ql[k] = valid ? v : 0.f;
+      }
+#pragma unroll
+      for (int j = 0; j < C::KRW; ++j) {
+        const float v = qrp[j * M::KSTEP];
+        qr[j] = valid ? v : 0.f;
       }
     }
   }
 
-  floatx16 acc[C::CB];
+  floatx16 acc[C::CBW];
 #pragma unroll
-  for (int cb = 0; cb < C::CB; ++cb) acc[cb] = floatx16{};
+  for (int k = 0; k < C::CBW; ++k) acc[k] = floatx16{};
   float m_run = -INFINITY;  // running (possibly stale, see kRescaleSlack) max of this head's log2 scores
   float l_run = 0.f;        // running sum of 2^(score - m_run)
 
   const int tr = M::row_token(col);  // stage token this lane's S row stands for
 
-  // Per-lane LDS byte offsets (bf16 path).  S operand: 16-byte chunk (2ks + h) of row tr; the
-  // low three chunk bits depend on ks only through ks & 3.
-  int klat[4] = {0, 0, 0, 0}, krope[4] = {0, 0, 0, 0};
-  int vtr[2][2] = {{0, 0}, {0, 0}};
+  // Per-lane LDS byte offsets (bf16 path).  Each is the offset of this lane's first operand;
+  // the others follow by XOR with a constant, because the swizzle XORs the low chunk bits and
+  // the operands of consecutive k-steps (column blocks) differ only in those bits.
+  //   S operand, latent: chunk 2k + h of the wave's slice of row tr  -> klat0 ^ 32 (k % NKL)
+  //   S operand, rope:   chunk 2(half*KRW + j) + h of row tr          -> krope0 ^ 32 j
+  //   V^T operand: lane group g = lane/16 serves columns 16*(g%2) + (lane%16) of a 32-column
+  //   block and tokens 8*(g/2) + 4*rb + [0, 4) of a 16-token k-step; its source lane
+  //   L = lane%16 loads columns 4*(L%4) .. +3 of token 8*(g/2) + 4*rb + L/4  -> vtr0[rb] ^ 64 (c % NVT)
+  constexpr int NKL = (C::MLS + 1) / 2 > 0 ? (C::MLS + 1) / 2 : 1;
+  constexpr int NVT = (C::MV >> 2) + 1;
+  static_assert(M::EPL != 8 || DR == 0 || 2 * C::KR <= C::MR + 1, "rope row must lie in one swizzle group");
+  const int lat_base = s * DL * ES + half * C::KLW * M::KSTEP * ES;  // wave's first latent byte in a row
+  const int v_base = s * DL * ES + half * C::CBW * 32 * ES;          // wave's first V column byte in a row
+  int klat0 = 0, krope0 = 0, vtr0[2] = {0, 0};
   if constexpr (M::EPL == 8) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      klat[q] = lds_off(tr, C::LW, (2 * q + h) * 16);
-      if constexpr (DR > 0) krope[q] = lds_off(tr, C::RW, (2 * q + h) * 16);
-    }
-    // V^T operand via transposed reads.  Lane group g = lane/16 serves columns 16*(g%2) + (lane%16)
-    // of a 32-column block and tokens 8*(g/2) + 4*rb + [0, 4) of a 16-token k-step; its source
-    // lane L = lane%16 loads columns 4*(L%4) .. +3 of token 8*(g/2) + 4*rb + L/4.
+    klat0 = lat_base + lds_off(tr, C::LW, C::MLS, h * 16);
+    if constexpr (DR > 0) krope0 = lds_off(tr, C::RW, C::MR, (2 * half * C::KRW + h) * 16);
     const int g16 = lane >> 4;
     const int L16 = lane & 15;
 #pragma unroll
-    for (int c1 = 0; c1 < 2; ++c1)
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
-        const int tt = 8 * (g16 >> 1) + 4 * rb + (L16 >> 2);
-        vtr[c1][rb] = lds_off(tt, C::VRB, (4 * c1 + 2 * (g16 & 1)) * 16 + (L16 & 3) * 8);
-      }
+    for (int rb = 0; rb < 2; ++rb) {
+      const int tt = 8 * (g16 >> 1) + 4 * rb + (L16 >> 2);
+      vtr0[rb] = v_base + lds_off(tt, C::VRB, C::MV, 2 * (g16 & 1) * 16 + (L16 & 3) * 8);
+    }
   }
 
-  // ---- prologue: stage 0
+  // ---- prologue: the first NBUF-1 stages
+  constexpr int NB = C::NBUF;
   const int nstage = (t_end - t_begin + kTile - 1) / kTile;
-  issue_stage(t_begin, smem);
-  finish_stage(smem);
+  char* const bufs[4] = {lds_b0, lds_b1, lds_b2, lds_b3};
+#pragma unroll
+  for (int n = 0; n < NB - 1; ++n)
+    if (n < nstage) issue_stage(t_begin + n * kTile, bufs[n]);
+  finish_stage(bufs[0]);
 
-  for (int n = 0; n < nstage; ++n) {
+  // one stage: `cur` holds stage n, `refill` receives stage n+NB-1 (it held stage n-1), `nxt`
+  // holds stage n+1 (fp8 writes its converted codes there)
+  auto stage_body = [&](const int n, char* const cur, char* const refill, char* const nxt)
+                        __attribute__((always_inline)) {
     const int stage0 = t_begin + n * kTile;
-    char* cur = smem + (n & 1) * C::BUF_AL;
-    char* nxt = smem + ((n + 1) & 1) * C::BUF_AL;
-    __builtin_amdgcn_s_waitcnt(0);   // this wave's copies of stage n have landed (all counters zero)
-    __syncthreads();                 // ... and everyone's; everyone is done with stage n-1's buffer
-    if (n + 1 < nstage) issue_stage(stage0 + kTile, nxt);
+    // wait until this wave's copies of stage n have landed: the loads of the (up to NB-2) later
+    // stages already issued may stay in flight; then the barrier makes every wave's copies
+    // visible and guarantees every wave is done with stage n-1's buffer, which is refilled next
+    if constexpr (KV == KV_FP8) {
+      __builtin_amdgcn_s_waitcnt(0);
+    } else {
+      const int later = min(nstage - 1 - n, NB - 2);
+      if (later >= 2 && NB >= 4)
+        wait_vmcnt<2 * C::DMA_MIN_PER_WAVE>();
+      else if (later >= 1 && NB >= 3)
+        wait_vmcnt<C::DMA_MIN_PER_WAVE>();
+      else
+        wait_vmcnt<0>();
+    }
+    lds_barrier();
+    if (n + NB - 1 < nstage) issue_stage(stage0 + (NB - 1) * kTile, refill);
 
-    // ---- S^T for this wave's set: rows = stage tokens (permuted), columns = 32 heads
+    // ---- S^T over this wave's k-steps: rows = stage tokens (permuted), columns = 32 heads
     floatx16 sl = floatx16{};
     floatx16 sr = floatx16{};
+    if constexpr (M::EPL == 8) {
+      // the offsets are re-derived inside every stage (the empty asm hides that they are loop
+      // invariant), so the compiler does not keep one register per operand address
+      int kl = klat0, kr = krope0;
+      asm volatile("" : "+v"(kl), "+v"(kr));
 #pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) {
-      Frag af;
-      const bool lat = KIND != KIND_LATENT || ks * M::KSTEP < DL;
-      if constexpr (M::EPL == 8) {
-        const int c0 = lat ? (s * DL) / 8 + 2 * ks : 2 * (ks - DL / 16);   // even chunk, lane bit excluded
-        const char* p = lat ? cur + C::LAT_OFF + klat[(c0 >> 1) & 3] + 16 * (c0 & ~7)
-                            : cur + C::ROPE_OFF + krope[(c0 >> 1) & 3] + 16 * (c0 & ~7);
-        af = __builtin_bit_cast(Frag, *reinterpret_cast<const uint4*>(p));
-      } else {
-        const int d0 = ks * M::KSTEP + h;
-        const char* p = lat ? cur + C::LAT_OFF + lds_off(tr, C::LW, (s * DL + d0) * ES)
-                            : cur + C::ROPE_OFF + lds_off(tr, C::RW > 0 ? C::RW : 32, (d0 - DL) * ES);
-        af = *reinterpret_cast<const float*>(p);
+      for (int k = 0; k < C::KLW; ++k) {
+        const int o = (kl ^ (32 * (k & (NKL - 1)))) + 32 * (k & ~(NKL - 1));
+        const Frag af = __builtin_bit_cast(Frag, *reinterpret_cast<const uint4*>(cur + C::LAT_OFF + o));
+        sl = M::mma(af, ql[k], sl);
+        if ((k & 3) == 3) __builtin_amdgcn_sched_barrier(0);  // bound the operand reads in flight
       }
-      if (KV == KV_FP8 && !lat)
-        sr = M::mma(af, qf[ks], sr);
-      else
-        sl = M::mma(af, qf[ks], sl);
-      if ((ks & 3) == 3) __builtin_amdgcn_sched_barrier(0);  // bound the operand reads in flight
+#pragma unroll
+      for (int j = 0; j < C::KRW; ++j) {
+        const Frag af = __builtin_bit_cast(Frag, *reinterpret_cast<const uint4*>(cur + C::ROPE_OFF + (kr ^ (32 * j))));
+        if constexpr (KV == KV_FP8)
+          sr = M::mma(af, qr[j], sr);
+        else
+          sl = M::mma(af, qr[j], sl);
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < C::KLW; ++k) {
+        const float af = *reinterpret_cast<const float*>(cur + C::LAT_OFF +
+                                                         lds_off(tr, C::LW, C::MLS, (s * DL + k * M::KSTEP + h) * ES));
+        sl = M::mma(af, ql[k], sl);
+        if ((k & 7) == 7) __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int j = 0; j < C::KRW; ++j) {
+        const float af = *reinterpret_cast<const float*>(cur + C::ROPE_OFF +
+                                                         lds_off(tr, C::RW, C::MR, (j * M::KSTEP + h) * ES));
+        sl = M::mma(af, qr[j], sl);
+      }
     }
 
-    // ---- online softmax (log2 domain) over this lane's 16 tokens and its partner's 16
-    float sv[16];
     float tok_scale[16];
-    float mt = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int tt = M::token_of(i, h);
-      float v;
-      if constexpr (KV == KV_FP8) {
-        tok_scale[i] = reinterpret_cast<const float*>(cur + C::SC_OFF)[tt];
-        v = (tok_scale[i] * sl[i] + sr[i]) * a.scale_log2;
-      } else {
-        tok_scale[i] = 1.f;
-        v = sl[i] * a.scale_log2;
+    for (int i = 0; i < 16; ++i)
+      tok_scale[i] = (KV == KV_FP8) ? reinterpret_cast<const float*>(cur + C::SC_OFF)[M::token_of(i, h)] : 1.f;
+    // fp8: the per-token scale multiplies the latent part of the score only
+    float sp[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sp[i] = (KV == KV_FP8) ? tok_scale[i] * sl[i] + sr[i] : sl[i];
+
+    if constexpr (SPLIT == 2) {
+      // each wave of the pair posts its partial scores (lane-contiguous 16-byte pieces) and adds
+      // its partner's; the barrier also keeps the next stage's posts behind this stage's reads
+      float* ex = lds_exch + (wave >> 1) * (2 * 16 * 64);
+      floatx4* mine = reinterpret_cast<floatx4*>(ex + half * 16 * 64);
+      const floatx4* other = reinterpret_cast<const floatx4*>(ex + (1 - half) * 16 * 64);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) mine[j * 64 + lane] = floatx4{sp[4 * j], sp[4 * j + 1], sp[4 * j + 2], sp[4 * j + 3]};
+      lds_barrier();
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const floatx4 o = other[j * 64 + lane];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sp[4 * j + e] += o[e];
       }
-      v = (stage0 + tt < t_end) ? v : -INFINITY;
-      sv[i] = v;
-      mt = fmaxf(mt, v);
     }
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
+
+    // ---- online softmax (log2 domain) over this lane's 16 tokens and its partner lane's 16.
+    // Rows past the unit's end exist only in its last stage.  The scale is positive, so the max
+    // is taken over the raw scores and each exponent is one fma.
+    if (stage0 + kTile > t_end) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sp[i] = (stage0 + M::token_of(i, h) < t_end) ? sp[i] : -INFINITY;
+    }
+    float mt = sp[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) mt = fmaxf(mt, sp[i]);
+    mt = fmaxf(mt, __shfl_xor(mt, 32)) * a.scale_log2;
     // raise the running max only when this stage's max exceeds it by more than the slack
     const bool raise = mt > m_run + kRescaleSlack;
     const float m_new = raise ? mt : m_run;
-    const float alpha = raise ? exp2f(m_run - m_new) : 1.f;   // 0 on the first stage
+    const float alpha = raise ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;  // 0 on the first stage
     const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    float psum = 0.f;
+    float sv[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      sv[i] = exp2f(sv[i] - m_use);
-      psum += sv[i];
-    }
-    psum += __shfl_xor(psum, 32);
-    if (n > 0 && __any(alpha != 1.f)) {   // rare; O is still zero on the first stage
+    for (int i = 0; i < 16; ++i) sv[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sp[i], a.scale_log2, -m_use));
+    if (n > 0 && __any(alpha != 1.f)) {  // rare; O is still zero on the first stage
 #pragma unroll
-      for (int cb = 0; cb < C::CB; ++cb) acc[cb] *= alpha;
+      for (int k = 0; k < C::CBW; ++k) acc[k] *= alpha;
     }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
 
-    // ---- P^T fragments (B operand of the PV MFMA); fp8 folds the token scale in here
+    // ---- P^T fragments (B operand of the PV MFMA) and the stage's row sum.  bf16: the sum is
+    // taken over the rounded P the PV product uses; fp8 folds the token scale into P (it scales
+    // V) and sums the unscaled probabilities.
     Frag pf[M::PSTEPS];
+    float psum = 0.f;
     if constexpr (M::EPL == 8) {
 #pragma unroll
       for (int p2 = 0; p2 < M::PSTEPS; ++p2) {
@@ -437,49 +565,87 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(DecodeArgs a) {
         for (int j = 0; j < 8; ++j) f[j] = (__bf16)(sv[8 * p2 + j] * tok_scale[8 * p2 + j]);
         pf[p2] = f;
       }
+      if constexpr (KV == KV_FP8) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) psum += sv[i];
+      } else {
+        typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+        const bf16x2_t one2 = {(__bf16)1.f, (__bf16)1.f};
+#pragma unroll
+        for (int p2 = 0; p2 < M::PSTEPS; ++p2)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            psum = __builtin_amdgcn_fdot2_f32_bf16(bf16x2_t{pf[p2][2 * j], pf[p2][2 * j + 1]}, one2, psum, false);
+      }
     } else {
 #pragma unroll
-      for (int p2 = 0; p2 < M::PSTEPS; ++p2) pf[p2] = sv[p2] * tok_scale[p2];
-    }
-
-    // ---- O^T += V^T . P^T
-    const char* vsrc = cur + C::V_REG;
-#pragma unroll
-    for (int cb = 0; cb < C::CB; ++cb) {
-#pragma unroll
       for (int p2 = 0; p2 < M::PSTEPS; ++p2) {
-        Frag af;
-        if constexpr (M::EPL == 8) {
-          const int cstat = 16 * p2 * C::VRB + 16 * ((s * DL) / 8 + ((4 * cb) & ~7));
-          const bf16x4_t lo = lds_read_tr(vsrc + vtr[cb & 1][0] + cstat);
-          const bf16x4_t hi = lds_read_tr(vsrc + vtr[cb & 1][1] + cstat);
-          af = bf16x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        } else {
-          const int tt = 2 * p2 + h;
-          af = *reinterpret_cast<const float*>(vsrc + lds_off(tt, C::VRB, (s * DL + cb * 32 + col) * ES));
-        }
-        acc[cb] = M::mma(af, pf[p2], acc[cb]);
+        pf[p2] = sv[p2];
+        psum += sv[p2];
       }
-      __builtin_amdgcn_sched_barrier(0);
     }
+    psum += __shfl_xor(psum, 32);
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
 
+    // ---- O^T += V^T . P^T over this wave's column blocks
+    if constexpr (M::EPL == 8) {
+      int v0 = vtr0[0], v1 = vtr0[1];
+      asm volatile("" : "+v"(v0), "+v"(v1));
+      const char* vs = cur + C::V_REG;
+#pragma unroll
+      for (int k = 0; k < C::CBW; ++k) {
+#pragma unroll
+        for (int p2 = 0; p2 < M::PSTEPS; ++p2) {
+          const int cstat = 16 * p2 * C::VRB + 64 * (k & ~(NVT - 1));
+          const int cx = 64 * (k & (NVT - 1));
+          const bf16x4_t lo = lds_read_tr(vs + (v0 ^ cx) + cstat);
+          const bf16x4_t hi = lds_read_tr(vs + (v1 ^ cx) + cstat);
+          acc[k] = M::mma(bf16x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]}, pf[p2], acc[k]);
+        }
+        if (k & 1) __builtin_amdgcn_sched_barrier(0);  // bound the operand reads in flight
+      }
+    } else {
+      const char* vsrc = cur + C::V_REG;
+#pragma unroll
+      for (int k = 0; k < C::CBW; ++k) {
+#pragma unroll
+        for (int p2 = 0; p2 < M::PSTEPS; ++p2) {
+          const int tt = 2 * p2 + h;
+          const Frag af =
+              *reinterpret_cast<const float*>(vsrc + lds_off(tt, C::VRB, C::MV, (s * DL + k * 32 + col) * ES));
+          acc[k] = M::mma(af, pf[p2], acc[k]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
     if (n + 1 < nstage) finish_stage(nxt);
+  };
+
+  for (int n0 = 0; n0 < nstage; n0 += NB) {
+    stage_body(n0, bufs[0], bufs[(NB - 1) % NB], bufs[1 % NB]);
+    if (n0 + 1 < nstage) stage_body(n0 + 1, bufs[1 % NB], bufs[0], bufs[2 % NB]);
+    if constexpr (NB > 2)
+      if (n0 + 2 < nstage) stage_body(n0 + 2, bufs[2 % NB], bufs[1], bufs[3 % NB]);
+    if constexpr (NB > 3)
+      if (n0 + 3 < nstage) stage_body(n0 + 3, bufs[3 % NB], bufs[2], bufs[4 % NB]);
   }
 
   // ---- epilogue: normalise; final output for unsplit sequences, partials otherwise
   const float inv_l = 1.f / l_run;
   const float lse_v = (m_run + log2f(l_run)) * kLn2;
   if (!valid) return;
+  const int c_wave = half * C::CBW * 32;  // first O column this wave holds
   if (nsplit == 1) {
     const size_t orow = (size_t)b * a.rows + row;
-    if (h == 0) a.lse[orow] = lse_v;
+    if (h == 0 && half == 0) a.lse[orow] = lse_v;
 #pragma unroll
-    for (int cb = 0; cb < C::CB; ++cb) {
+    for (int k = 0; k < C::CBW; ++k) {
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
-        const int c = cb * 32 + 8 * g4 + 4 * h;
-        const float o0 = acc[cb][4 * g4 + 0] * inv_l, o1 = acc[cb][4 * g4 + 1] * inv_l;
-        const float o2 = acc[cb][4 * g4 + 2] * inv_l, o3 = acc[cb][4 * g4 + 3] * inv_l;
+        const int c = c_wave + k * 32 + 8 * g4 + 4 * h;
+        const float o0 = acc[k][4 * g4 + 0] * inv_l, o1 = acc[k][4 * g4 + 1] * inv_l;
+        const float o2 = acc[k][4 * g4 + 2] * inv_l, o3 = acc[k][4 * g4 + 3] * inv_l;
         if (a.out_bf16) {
           __bf16* dst = static_cast<__bf16*>(a.out) + orow * DL + c;
           bf16x4_t v = {(__bf16)o0, (__bf16)o1, (__bf16)o2, (__bf16)o3};
@@ -492,63 +658,59 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(DecodeArgs a) {
     }
   } else {
     const size_t prow = (size_t)unit * a.rows + row;
-    if (h == 0) a.part_lse[prow] = lse_v;
+    if (h == 0 && half == 0) a.part_lse[prow] = lse_v;
 #pragma unroll
-    for (int cb = 0; cb < C::CB; ++cb) {
+    for (int k = 0; k < C::CBW; ++k) {
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
-        const int c = cb * 32 + 8 * g4 + 4 * h;
+        const int c = c_wave + k * 32 + 8 * g4 + 4 * h;
         float* dst = a.part_out + prow * DL + c;
-        *reinterpret_cast<float4*>(dst) =
-            make_float4(acc[cb][4 * g4] * inv_l, acc[cb][4 * g4 + 1] * inv_l, acc[cb][4 * g4 + 2] * inv_l,
-                        acc[cb][4 * g4 + 3] * inv_l);
+        *reinterpret_cast<float4*>(dst) = make_float4(acc[k][4 * g4] * inv_l, acc[k][4 * g4 + 1] * inv_l,
+                                                      acc[k][4 * g4 + 2] * inv_l, acc[k][4 * g4 + 3] * inv_l);
       }
     }
   }
 }
 
-template <int KV, int DL, int DR, int KIND, int NSETS, int WAVES>
+template <int KV, int DL, int DR, int KIND, int NSETS, int HB, int SPLIT>
 int run(const DecodeArgs& a, void* stream) {
-  using C = Cfg<KV, DL, DR, KIND, NSETS, WAVES>;
-  if (a.nsets != NSETS || a.nsets * a.hblocks != WAVES) return -1;
-  auto fn = decode_kernel<KV, DL, DR, KIND, NSETS, WAVES>;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
-                                     C::LDS_BYTES);
-  if (e != hipSuccess) return (int)e;
+  if (a.nsets != NSETS || a.hblocks != HB) return -1;
+  auto fn = decode_kernel<KV, DL, DR, KIND, NSETS, HB, SPLIT>;
   const int units8 = (a.max_units + 7) / 8 * 8;
   const dim3 grid(units8 * a.wg_per_unit);
-  hipLaunchKernelGGL(fn, grid, dim3(C::THREADS), C::LDS_BYTES, static_cast<hipStream_t>(stream), a);
+  hipLaunchKernelGGL(fn, grid, dim3(NSETS * HB * SPLIT * kWaveSize), 0, static_cast<hipStream_t>(stream), a,
+                     a.block_table);
   return (int)hipGetLastError();
 }
 
 // ------------------------------------------------------------------------------------------
-// the instantiated shapes: (kv dtype, d_latent, d_rope, kind, sets per work group, waves)
+// the instantiated shapes: (kv dtype, d_latent, d_rope, kind, sets per work group, 32-head
+// blocks per set, waves per head block)
 // ------------------------------------------------------------------------------------------
-#define LD_SHAPES(X)                                                                                   \
-  /* MLA: 128 / 64 / 32 heads */                                                                       \
-  X(KV_BF16, 512, 64, KIND_LATENT, 1, 4) X(KV_BF16, 512, 64, KIND_LATENT, 1, 2)                         \
-  X(KV_BF16, 512, 64, KIND_LATENT, 1, 1) X(KV_FP8, 512, 64, KIND_LATENT, 1, 4)                          \
-  X(KV_FP8, 512, 64, KIND_LATENT, 1, 2) X(KV_FP8, 512, 64, KIND_LATENT, 1, 1)                           \
-  /* GLA-2 (2 groups x 64 heads), GLA-4, one group */                                                  \
-  X(KV_BF16, 256, 64, KIND_LATENT, 2, 4) X(KV_BF16, 256, 64, KIND_LATENT, 4, 4)                         \
-  X(KV_BF16, 256, 64, KIND_LATENT, 1, 4) X(KV_FP8, 256, 64, KIND_LATENT, 2, 4)                          \
-  X(KV_FP8, 256, 64, KIND_LATENT, 4, 4) X(KV_FP8, 256, 64, KIND_LATENT, 1, 4)                           \
-  /* MLRA-4 (two branches of 128 heads per work group), one branch */                                  \
-  X(KV_BF16, 128, 64, KIND_LATENT, 2, 8) X(KV_BF16, 128, 64, KIND_LATENT, 1, 4)                         \
-  X(KV_FP8, 128, 64, KIND_LATENT, 2, 8) X(KV_FP8, 128, 64, KIND_LATENT, 1, 4)                           \
-  /* small latent shapes: up to 32 heads per set */                                                    \
-  X(KV_F32, 64, 16, KIND_LATENT, 1, 1) X(KV_F32, 64, 16, KIND_LATENT, 2, 2)                             \
-  X(KV_F32, 64, 16, KIND_LATENT, 4, 4) X(KV_BF16, 64, 16, KIND_LATENT, 1, 1)                            \
-  X(KV_BF16, 64, 16, KIND_LATENT, 2, 2) X(KV_BF16, 64, 16, KIND_LATENT, 4, 4)                           \
-  X(KV_FP8, 64, 16, KIND_LATENT, 1, 1) X(KV_FP8, 64, 16, KIND_LATENT, 2, 2)                             \
-  X(KV_FP8, 64, 16, KIND_LATENT, 4, 4)                                                                  \
-  /* GQA: 4 kv heads (K and V) per work group; GTA: 8; MQA: one kv head */                     \
-  X(KV_BF16, 128, 0, KIND_SHARED, 4, 4) X(KV_BF16, 128, 0, KIND_SHARED, 2, 2)                           \
-  X(KV_BF16, 128, 0, KIND_SHARED, 1, 2) X(KV_BF16, 128, 0, KIND_SHARED, 1, 1)                           \
-  X(KV_BF16, 128, 0, KIND_TIED, 8, 8) X(KV_BF16, 128, 0, KIND_TIED, 4, 4)                               \
-  X(KV_BF16, 128, 0, KIND_TIED, 1, 2) X(KV_BF16, 128, 0, KIND_TIED, 1, 1)                               \
-  X(KV_F32, 64, 0, KIND_SHARED, 4, 4) X(KV_F32, 64, 0, KIND_SHARED, 1, 1)                               \
-  X(KV_F32, 64, 0, KIND_TIED, 4, 4) X(KV_F32, 64, 0, KIND_TIED, 1, 1)
+#define LD_SHAPES(X)                                                                          \
+  /* MLA: 128 / 64 heads */                                                                   \
+  X(KV_BF16, 512, 64, KIND_LATENT, 1, 4, 2) X(KV_BF16, 512, 64, KIND_LATENT, 1, 2, 2)          \
+  X(KV_FP8, 512, 64, KIND_LATENT, 1, 4, 2)                                                    \
+  /* GLA-2 (2 groups x 64 heads), GLA-4 (4 groups x 32 heads), one group of 128 heads */      \
+  X(KV_BF16, 256, 64, KIND_LATENT, 2, 2, 2) X(KV_BF16, 256, 64, KIND_LATENT, 4, 1, 1)          \
+  X(KV_BF16, 256, 64, KIND_LATENT, 1, 4, 2) X(KV_FP8, 256, 64, KIND_LATENT, 2, 2, 2)           \
+  X(KV_FP8, 256, 64, KIND_LATENT, 4, 1, 1) X(KV_FP8, 256, 64, KIND_LATENT, 1, 4, 2)            \
+  /* MLRA-4 (two branches of 128 heads per work group), one branch */                         \
+  X(KV_BF16, 128, 64, KIND_LATENT, 2, 4, 1) X(KV_BF16, 128, 64, KIND_LATENT, 1, 4, 1)          \
+  X(KV_FP8, 128, 64, KIND_LATENT, 2, 4, 1) X(KV_FP8, 128, 64, KIND_LATENT, 1, 4, 1)            \
+  /* small latent shapes: up to 32 heads per set */                                           \
+  X(KV_F32, 64, 16, KIND_LATENT, 1, 1, 1) X(KV_F32, 64, 16, KIND_LATENT, 2, 1, 1)              \
+  X(KV_F32, 64, 16, KIND_LATENT, 4, 1, 1) X(KV_BF16, 64, 16, KIND_LATENT, 1, 1, 1)             \
+  X(KV_BF16, 64, 16, KIND_LATENT, 2, 1, 1) X(KV_BF16, 64, 16, KIND_LATENT, 4, 1, 1)            \
+  X(KV_FP8, 64, 16, KIND_LATENT, 1, 1, 1) X(KV_FP8, 64, 16, KIND_LATENT, 2, 1, 1)              \
+  X(KV_FP8, 64, 16, KIND_LATENT, 4, 1, 1)                                                      \
+  /* GQA: 4 kv heads (K and V) per work group; GTA: 8; MQA: one kv head of 64 or 32 heads */  \
+  X(KV_BF16, 128, 0, KIND_SHARED, 4, 1, 1) X(KV_BF16, 128, 0, KIND_SHARED, 2, 1, 1)            \
+  X(KV_BF16, 128, 0, KIND_SHARED, 1, 2, 1) X(KV_BF16, 128, 0, KIND_SHARED, 1, 1, 1)            \
+  X(KV_BF16, 128, 0, KIND_TIED, 8, 1, 1) X(KV_BF16, 128, 0, KIND_TIED, 4, 1, 1)                \
+  X(KV_BF16, 128, 0, KIND_TIED, 1, 2, 1) X(KV_BF16, 128, 0, KIND_TIED, 1, 1, 1)                \
+  X(KV_F32, 64, 0, KIND_SHARED, 4, 1, 1) X(KV_F32, 64, 0, KIND_SHARED, 1, 1, 1)                \
+  X(KV_F32, 64, 0, KIND_TIED, 4, 1, 1) X(KV_F32, 64, 0, KIND_TIED, 1, 1, 1)
 
 int kv_code(const ld_problem& p) { return p.kv_dtype == LD_FP8_E4M3 ? KV_FP8 : p.kv_dtype == LD_BF16 ? KV_BF16 : KV_F32; }
 int kind_code(const ld_problem& p) {
@@ -558,10 +720,10 @@ int kind_code(const ld_problem& p) {
 
 }  // namespace
 
-bool decode_instantiated(const ld_problem& p, int nsets, int waves) {
+bool decode_instantiated(const ld_problem& p, int nsets, int hblocks) {
   const int kv = kv_code(p), kind = kind_code(p), dl = p.d_latent, dr = p.d_rope;
-#define LD_MATCH(KV_, DL_, DR_, KIND_, NS_, W_) \
-  if (kv == KV_ && dl == DL_ && dr == DR_ && kind == KIND_ && nsets == NS_ && waves == W_) return true;
+#define LD_MATCH(KV_, DL_, DR_, KIND_, NS_, HB_, SP_) \
+  if (kv == KV_ && dl == DL_ && dr == DR_ && kind == KIND_ && nsets == NS_ && hblocks == HB_) return true;
   LD_SHAPES(LD_MATCH)
 #undef LD_MATCH
   return false;
@@ -569,10 +731,9 @@ bool decode_instantiated(const ld_problem& p, int nsets, int waves) {
 
 int launch_decode(const ld_problem& p, const DecodeArgs& a, void* stream) {
   const int kv = kv_code(p), kind = kind_code(p), dl = p.d_latent, dr = p.d_rope;
-  const int nsets = a.nsets, waves = a.nsets * a.hblocks;
-#define LD_RUN(KV_, DL_, DR_, KIND_, NS_, W_) \
-  if (kv == KV_ && dl == DL_ && dr == DR_ && kind == KIND_ && nsets == NS_ && waves == W_) \
-    return run<KV_, DL_, DR_, KIND_, NS_, W_>(a, stream);
+#define LD_RUN(KV_, DL_, DR_, KIND_, NS_, HB_, SP_)                                               \
+  if (kv == KV_ && dl == DL_ && dr == DR_ && kind == KIND_ && a.nsets == NS_ && a.hblocks == HB_) \
+    return run<KV_, DL_, DR_, KIND_, NS_, HB_, SP_>(a, stream);
   LD_SHAPES(LD_RUN)
 #undef LD_RUN
   return -1;

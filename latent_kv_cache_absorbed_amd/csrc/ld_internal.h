@@ -94,9 +94,9 @@ int launch_combine_rows(int32_t num_rows, int32_t d_v, int32_t max_splits, const
                         void* stream);
 // Returns hipError_t, or -1 when no kernel is built for the shape.
 int launch_decode(const ld_problem& p, const DecodeArgs& a, void* stream);
-// Whether a decode kernel is built for p's dtype/dims/kind with `nsets` sets and `waves` waves
-// per work group.
-bool decode_instantiated(const ld_problem& p, int nsets, int waves);
+// Whether a decode kernel is built for p's dtype/dims/kind with `nsets` sets per work group and
+// `hblocks` 32-head blocks per set.
+bool decode_instantiated(const ld_problem& p, int nsets, int hblocks);
 int device_cu_count();
 
 }  // namespace ld

@@ -48,7 +48,7 @@ def test_supported_problems_check_ok(kw):
     (dict(batch=-1), SHAPE), (dict(heads=0), SHAPE), (dict(variant="mla", groups=2), SHAPE),
     (dict(variant="gla", groups=3, d_latent=256), SHAPE), (dict(variant="gqa", heads=64, groups=8, d_latent=128), SHAPE),
     (dict(d_rope=0), SHAPE), (dict(page_size=0), SHAPE), (dict(num_pages=0), SHAPE), (dict(num_splits=-2), SHAPE),
-    (dict(scale=float("nan")), SHAPE), (dict(max_pages_per_seq=1 << 20, page_size=1 << 12), SHAPE),
+    (dict(scale=float("nan")), SHAPE), (dict(scale=0.0), SHAPE), (dict(scale=-0.1), SHAPE), (dict(max_pages_per_seq=1 << 20, page_size=1 << 12), SHAPE),
     (dict(q_dtype="f32"), DTYPE), (dict(kv_dtype="f32"), DTYPE), (dict(out_dtype="fp8_e4m3"), DTYPE),
     (dict(variant="gqa", heads=64, groups=8, d_latent=128, d_rope=0, kv_dtype="fp8_e4m3"), DTYPE),
     (dict(d_latent=384), UNSUP), (dict(d_rope=32), UNSUP), (dict(heads=256), UNSUP),
