@@ -48,10 +48,11 @@ WsLayout ws_layout(const ld_problem& p, int num_cus) {
   off = round256(off + (size_t)w.max_units * sizeof(Unit));
   w.seqs = off;
   off = round256(off + (size_t)p.batch * 2 * sizeof(int32_t));
+  const size_t slots = (size_t)w.max_units * p.num_groups * launch_shape(p).hblocks * 32;
   w.part_lse = off;
-  off = round256(off + (size_t)w.max_units * w.rows * sizeof(float));
+  off = round256(off + slots * sizeof(float));
   w.part_out = off;
-  off = round256(off + (size_t)w.max_units * w.rows * w.d_v * sizeof(float));
+  off = round256(off + slots * w.d_v * (p.out_dtype == LD_BF16 ? 2 : 4));
   w.total = off;
   return w;
 }
@@ -249,7 +250,7 @@ DecodeArgs decode_args(const ld_problem* p, const WsLayout& w, void* workspace) 
   a.units = reinterpret_cast<const Unit*>(ws + w.units);
   a.seqs = reinterpret_cast<const int32_t*>(ws + w.seqs);
   a.part_lse = reinterpret_cast<float*>(ws + w.part_lse);
-  a.part_out = reinterpret_cast<float*>(ws + w.part_out);
+  a.part_out = ws + w.part_out;
   a.batch = p->batch;
   a.heads = p->num_q_heads;
   a.groups = p->num_groups;
@@ -263,6 +264,7 @@ DecodeArgs decode_args(const ld_problem* p, const WsLayout& w, void* workspace) 
   a.wg_per_unit = s.wg_per_unit;
   a.max_units = w.max_units;
   a.out_bf16 = p->out_dtype == LD_BF16;
+  a.part_bf16 = a.out_bf16;
   a.mlra = p->variant == LD_VARIANT_MLRA;
   a.scale_log2 = p->softmax_scale * 1.4426950408889634f;
   return a;

@@ -47,6 +47,7 @@ typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
 enum KvT : int { KV_F32 = 0, KV_BF16 = 1, KV_FP8 = 2 };
 
 constexpr float kLn2 = 0.69314718055994530942f;
+constexpr int kPageCap = 512;  // block-table entries of a unit staged in LDS
 // The running max is raised only when a stage's max exceeds it by more than this (log2 units),
 // so O is rescaled rarely; scores then stay <= 2^8 above the stale max, far from overflow.
 constexpr float kRescaleSlack = 8.f;
@@ -120,6 +121,15 @@ struct Mma<KV_F32> {
 
 __device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
 
+// Value of lane l ^ 32 (the other half of the wave), through v_permlane32_swap (a VALU op)
+// rather than an LDS round trip: swapping a copy of x with itself leaves lanes 32..63 of the
+// first result holding lanes 0..31 of x, and lanes 0..31 of the second holding lanes 32..63.
+__device__ __forceinline__ float xor32(float x) {
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __builtin_bit_cast(float, (__lane_id() < 32) ? r[1] : r[0]);
+}
+
 constexpr int ilog2(int x) { return x <= 1 ? 0 : 1 + ilog2(x / 2); }
 constexpr bool pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
 constexpr int cmin(int a, int b) { return a < b ? a : b; }
@@ -187,16 +197,19 @@ struct Cfg {
   static constexpr int BUF_AL = (BUF + 127) / 128 * 128;
   static constexpr int EXCH = (SPLIT == 2) ? WAVES * 16 * 64 * 4 : 16;   // partial-score exchange
   // stage buffers: as many as fit (up to 4); the fp8 path stages through registers and keeps two
-  static constexpr int NB_FIT = (160 * 1024 - EXCH) / BUF_AL;
+  static constexpr int NB_FIT = (160 * 1024 - EXCH - 4 * kPageCap) / BUF_AL;
   static constexpr int NBUF = (KV == KV_FP8) ? 2 : cmin(NB_FIT, 4);
-  static constexpr int LDS_TOTAL = 2 * BUF_AL + (NBUF > 2 ? BUF_AL : 128) + (NBUF > 3 ? BUF_AL : 128) + EXCH;
+  static constexpr int LDS_TOTAL =
+      2 * BUF_AL + (NBUF > 2 ? BUF_AL : 128) + (NBUF > 3 ? BUF_AL : 128) + EXCH + 4 * kPageCap;
   static constexpr int VRB = (KIND == KIND_SHARED) ? VW : LW;   // row bytes of the V source region
   static constexpr int V_REG = (KIND == KIND_SHARED) ? V_OFF : LAT_OFF;
   static constexpr int FP8_ITEMS = kTile * NSETS * DL / 16;      // 16-code pieces of an fp8 stage
   static constexpr int FP8_PER_THREAD = (KV == KV_FP8) ? (FP8_ITEMS + THREADS - 1) / THREADS : 1;
   // 1 KB DMA blocks per stage (all regions) and the fewest any wave issues per stage
   static constexpr int DMA_BLOCKS = (KV == KV_FP8) ? kTile * RW / 1024 : kTile * (LW + RW + VW) / 1024;
-  static constexpr int DMA_MIN_PER_WAVE = DMA_BLOCKS / WAVES;
+  static constexpr bool PP = (WAVES == 8) && (KV != KV_FP8);     // see the stage loop
+  static constexpr int DMA_WAVES = PP ? WAVES / 2 : WAVES;         // waves that issue copies
+  static constexpr int DMA_MIN_PER_WAVE = DMA_BLOCKS / DMA_WAVES;
   static_assert(DL % 32 == 0 && DL % M::KSTEP == 0 && DR % M::KSTEP == 0, "unsupported dims");
   static_assert(KL % SPLIT == 0 && KR % SPLIT == 0 && CB % SPLIT == 0, "dims must split evenly");
   static_assert(SPLIT == 1 || M::EPL == 8, "split waves need the bf16 operand path");
@@ -253,6 +266,7 @@ __global__ __launch_bounds__(NSETS* HB* SPLIT * 64) void decode_kernel(DecodeArg
   __shared__ __attribute__((aligned(128))) char lds_b2[C::NBUF > 2 ? C::BUF_AL : 128];
   __shared__ __attribute__((aligned(128))) char lds_b3[C::NBUF > 3 ? C::BUF_AL : 128];
   __shared__ __attribute__((aligned(16))) float lds_exch[C::EXCH / 4];
+  __shared__ int lds_pages[kPageCap];
 
   // XCD-aware mapping: all work groups of one unit land on the same XCD (ids = unit mod 8)
   const int x = blockIdx.x;
@@ -281,8 +295,15 @@ __global__ __launch_bounds__(NSETS* HB* SPLIT * 64) void decode_kernel(DecodeArg
   const bool valid = head_in_set < a.heads_per_set;
   const int head = (a.mlra ? 0 : gs * a.heads_per_set) + (valid ? head_in_set : 0);
   const int row = a.mlra ? head * G + gs : head;
-  const int32_t* __restrict__ bt_row = block_table + (size_t)b * a.max_pages;  // read with scalar loads
+  const int32_t* __restrict__ bt_row = block_table + (size_t)b * a.max_pages;
   const int page_size = a.page_size;
+  // The unit's first kPageCap block-table entries are staged in LDS up front, so that issuing a
+  // stage's copies waits for an LDS read rather than a dependent scalar load from memory.
+  const int first_page = t_begin / page_size;
+  const int unit_pages = t_end > t_begin ? (t_end - 1) / page_size - first_page + 1 : 0;
+  for (int i = threadIdx.x; i < unit_pages && i < kPageCap; i += C::THREADS)
+    lds_pages[i] = clampi(bt_row[first_page + i], 0, a.num_pages - 1);
+  __syncthreads();
 
   // global row geometry (bytes): latent variants store [G latents | rope] per token (fp8: codes
   // only, the rope key lives in its own pool); GQA/MQA/GTA store [G kv heads][DL] per token
@@ -294,11 +315,13 @@ __global__ __launch_bounds__(NSETS* HB* SPLIT * 64) void decode_kernel(DecodeArg
   float pre_sc = 0.f;
   auto issue_stage = [&](int stage0, char* buf) {
     // every token of a stage lies in one page (stages are page aligned and page_size % 32 == 0)
-    const int page = clampi(bt_row[stage0 / page_size], 0, a.num_pages - 1);
+    const int pi = stage0 / page_size - first_page;
+    const int page = pi < kPageCap ? __builtin_amdgcn_readfirstlane(lds_pages[pi])
+                                   : clampi(bt_row[stage0 / page_size], 0, a.num_pages - 1);
     const size_t r0 = (size_t)page * page_size + (stage0 % page_size);
     const int tlast = t_end - 1 - stage0;  // rows past the unit's end repeat its last row
     if constexpr (KV != KV_FP8) {
-      dma_region<C::LW, C::MLS, WAVES, 0>(buf + C::LAT_OFF, wave, lane,
+      dma_region<C::LW, C::MLS, C::DMA_WAVES, 0>(buf + C::LAT_OFF, wave, lane,
                                 [&](int t) { return kbase + (r0 + min(t, tlast)) * (size_t)grow_bytes; },
                                 [&](int cb) {
                                   const int s2 = cb / (DL * ES);
@@ -323,18 +346,18 @@ __global__ __launch_bounds__(NSETS* HB* SPLIT * 64) void decode_kernel(DecodeArg
     if constexpr (KIND == KIND_LATENT && DR > 0) {
       if constexpr (KV == KV_FP8) {
         const char* rbase = static_cast<const char*>(a.rope);
-        dma_region<C::RW, C::MR, WAVES, 0>(buf + C::ROPE_OFF, wave, lane,
+        dma_region<C::RW, C::MR, C::DMA_WAVES, 0>(buf + C::ROPE_OFF, wave, lane,
                                  [&](int t) { return rbase + (r0 + min(t, tlast)) * (size_t)(DR * 2); },
                                  [&](int cb) { return cb; });
       } else {
-        dma_region<C::RW, C::MR, WAVES, kTile * C::LW / 1024>(buf + C::ROPE_OFF, wave, lane,
+        dma_region<C::RW, C::MR, C::DMA_WAVES, kTile * C::LW / 1024>(buf + C::ROPE_OFF, wave, lane,
                                  [&](int t) { return kbase + (r0 + min(t, tlast)) * (size_t)grow_bytes; },
                                  [&](int cb) { return G * DL * ES + cb; });
       }
     }
     if constexpr (KIND == KIND_SHARED) {
       const char* vbase_g = static_cast<const char*>(a.v);
-      dma_region<C::VW, C::MV, WAVES, kTile *(C::LW + C::RW) / 1024>(buf + C::V_OFF, wave, lane,
+      dma_region<C::VW, C::MV, C::DMA_WAVES, kTile *(C::LW + C::RW) / 1024>(buf + C::V_OFF, wave, lane,
                                [&](int t) { return vbase_g + (r0 + min(t, tlast)) * (size_t)grow_bytes; },
                                [&](int cb) {
                                  const int s2 = cb / (DL * ES);
@@ -436,33 +459,20 @@ __global__ __launch_bounds__(NSETS* HB* SPLIT * 64) void decode_kernel(DecodeArg
   constexpr int NB = C::NBUF;
   const int nstage = (t_end - t_begin + kTile - 1) / kTile;
   char* const bufs[4] = {lds_b0, lds_b1, lds_b2, lds_b3};
+  // with the half-stage offset (see the stage loop) only the early half of the waves copies
+  const bool late = C::PP && wave >= WAVES / 2;  // wave-uniform
+  if (!late) {
 #pragma unroll
-  for (int n = 0; n < NB - 1; ++n)
-    if (n < nstage) issue_stage(t_begin + n * kTile, bufs[n]);
+    for (int n = 0; n < NB - 1; ++n)
+      if (n < nstage) issue_stage(t_begin + n * kTile, bufs[n]);
+  }
   finish_stage(bufs[0]);
 
-  // one stage: `cur` holds stage n, `refill` receives stage n+NB-1 (it held stage n-1), `nxt`
-  // holds stage n+1 (fp8 writes its converted codes there)
-  auto stage_body = [&](const int n, char* const cur, char* const refill, char* const nxt)
-                        __attribute__((always_inline)) {
-    const int stage0 = t_begin + n * kTile;
-    // wait until this wave's copies of stage n have landed: the loads of the (up to NB-2) later
-    // stages already issued may stay in flight; then the barrier makes every wave's copies
-    // visible and guarantees every wave is done with stage n-1's buffer, which is refilled next
-    if constexpr (KV == KV_FP8) {
-      __builtin_amdgcn_s_waitcnt(0);
-    } else {
-      const int later = min(nstage - 1 - n, NB - 2);
-      if (later >= 2 && NB >= 4)
-        wait_vmcnt<2 * C::DMA_MIN_PER_WAVE>();
-      else if (later >= 1 && NB >= 3)
-        wait_vmcnt<C::DMA_MIN_PER_WAVE>();
-      else
-        wait_vmcnt<0>();
-    }
-    lds_barrier();
-    if (n + NB - 1 < nstage) issue_stage(stage0 + (NB - 1) * kTile, refill);
-
+  // The work on a stage has two parts.  part_s: this wave's (partial) scores, into sp; with
+  // SPLIT = 2 they are posted for the partner wave.  part_pv: (the partner's half added) the online
+  // softmax and O += P.V.  A barrier separates the two parts of a stage.
+  float sp[16];
+  auto part_s = [&](char* const cur) __attribute__((always_inline)) {
     // ---- S^T over this wave's k-steps: rows = stage tokens (permuted), columns = 32 heads
     floatx16 sl = floatx16{};
     floatx16 sr = floatx16{};
@@ -507,19 +517,22 @@ __global__ __launch_bounds__(NSETS* HB* SPLIT * 64) void decode_kernel(DecodeArg
     for (int i = 0; i < 16; ++i)
       tok_scale[i] = (KV == KV_FP8) ? reinterpret_cast<const float*>(cur + C::SC_OFF)[M::token_of(i, h)] : 1.f;
     // fp8: the per-token scale multiplies the latent part of the score only
-    float sp[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) sp[i] = (KV == KV_FP8) ? tok_scale[i] * sl[i] + sr[i] : sl[i];
 
     if constexpr (SPLIT == 2) {
-      // each wave of the pair posts its partial scores (lane-contiguous 16-byte pieces) and adds
-      // its partner's; the barrier also keeps the next stage's posts behind this stage's reads
-      float* ex = lds_exch + (wave >> 1) * (2 * 16 * 64);
-      floatx4* mine = reinterpret_cast<floatx4*>(ex + half * 16 * 64);
-      const floatx4* other = reinterpret_cast<const floatx4*>(ex + (1 - half) * 16 * 64);
+      // post this wave's partial scores (lane-contiguous 16-byte pieces) for the partner
+      floatx4* mine = reinterpret_cast<floatx4*>(lds_exch + (wave >> 1) * (2 * 16 * 64) + half * 16 * 64);
 #pragma unroll
       for (int j = 0; j < 4; ++j) mine[j * 64 + lane] = floatx4{sp[4 * j], sp[4 * j + 1], sp[4 * j + 2], sp[4 * j + 3]};
-      lds_barrier();
+    }
+  };
+  auto part_pv = [&](const int n, char* const cur) __attribute__((always_inline)) {
+    const int stage0 = t_begin + n * kTile;
+    if constexpr (SPLIT == 2) {
+      // add the partner's partial scores (posted before the barrier that precedes this part)
+      const floatx4* other =
+          reinterpret_cast<const floatx4*>(lds_exch + (wave >> 1) * (2 * 16 * 64) + (1 - half) * 16 * 64);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const floatx4 o = other[j * 64 + lane];
@@ -527,6 +540,10 @@ __global__ __launch_bounds__(NSETS* HB* SPLIT * 64) void decode_kernel(DecodeArg
         for (int e = 0; e < 4; ++e) sp[4 * j + e] += o[e];
       }
     }
+    float tok_scale[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      tok_scale[i] = (KV == KV_FP8) ? reinterpret_cast<const float*>(cur + C::SC_OFF)[M::token_of(i, h)] : 1.f;
 
     // ---- online softmax (log2 domain) over this lane's 16 tokens and its partner lane's 16.
     // Rows past the unit's end exist only in its last stage.  The scale is positive, so the max
@@ -538,7 +555,7 @@ __global__ __launch_bounds__(NSETS* HB* SPLIT * 64) void decode_kernel(DecodeArg
     float mt = sp[0];
 #pragma unroll
     for (int i = 1; i < 16; ++i) mt = fmaxf(mt, sp[i]);
-    mt = fmaxf(mt, __shfl_xor(mt, 32)) * a.scale_log2;
+    mt = fmaxf(mt, xor32(mt)) * a.scale_log2;
     // raise the running max only when this stage's max exceeds it by more than the slack
     const bool raise = mt > m_run + kRescaleSlack;
     const float m_new = raise ? mt : m_run;
@@ -584,7 +601,7 @@ __global__ __launch_bounds__(NSETS* HB* SPLIT * 64) void decode_kernel(DecodeArg
         psum += sv[p2];
       }
     }
-    psum += __shfl_xor(psum, 32);
+    psum += xor32(psum);
     l_run = l_run * alpha + psum;
     m_run = m_new;
 
@@ -619,31 +636,70 @@ __global__ __launch_bounds__(NSETS* HB* SPLIT * 64) void decode_kernel(DecodeArg
         __builtin_amdgcn_sched_barrier(0);
       }
     }
+  };
+
+  // With eight waves (two per SIMD) the two halves of the work group run half a stage apart, so
+  // that on every SIMD one wave's score MFMAs overlap the other wave's softmax and P.V.  Every
+  // wave runs the same program (barrier, part_s(n), barrier, part_pv(n) per stage); the late half
+  // passes one extra barrier first, the early half one extra barrier last, so with barriers
+  // counted across the work group the early half computes part_s(n) after barrier 2n and
+  // part_pv(n) after 2n+1, the late half one barrier later.  Only the early half issues the
+  // copies: it waits for its copies of stage n before barrier 2n (the first read of stage n comes
+  // after it), and refills stage n-1's buffer after barrier 2n+1 (its last read, the late half's
+  // part_pv(n-1), comes before it).  Without the offset (fewer waves, or the fp8 cache, which is
+  // staged through registers) every wave copies and the refill follows the first barrier.
+  constexpr bool PP = C::PP;
+  auto wait_stage = [&](const int n) __attribute__((always_inline)) {
+    // this wave's copies of stage n have landed; those of the (up to NB-2) later stages already
+    // issued may stay in flight
+    if constexpr (KV == KV_FP8) {
+      __builtin_amdgcn_s_waitcnt(0);
+    } else {
+      const int later = min(nstage - 1 - n, NB - 2);
+      if (later >= 2 && NB >= 4)
+        wait_vmcnt<2 * C::DMA_MIN_PER_WAVE>();
+      else if (later >= 1 && NB >= 3)
+        wait_vmcnt<C::DMA_MIN_PER_WAVE>();
+      else
+        wait_vmcnt<0>();
+    }
+  };
+  auto iter = [&](const int n, char* const cur, char* const refill, char* const nxt) __attribute__((always_inline)) {
+    if (!late) wait_stage(n);
+    lds_barrier();
+    if (!PP && n + NB - 1 < nstage) issue_stage(t_begin + (n + NB - 1) * kTile, refill);
+    part_s(cur);
+    if constexpr (PP || SPLIT == 2) lds_barrier();
+    if (PP && !late && n + NB - 1 < nstage) issue_stage(t_begin + (n + NB - 1) * kTile, refill);
+    part_pv(n, cur);
     if (n + 1 < nstage) finish_stage(nxt);
   };
 
+  if (late) lds_barrier();
+  // unrolled over the stage buffers, so that every LDS access names its buffer statically
   for (int n0 = 0; n0 < nstage; n0 += NB) {
-    stage_body(n0, bufs[0], bufs[(NB - 1) % NB], bufs[1 % NB]);
-    if (n0 + 1 < nstage) stage_body(n0 + 1, bufs[1 % NB], bufs[0], bufs[2 % NB]);
+    iter(n0, bufs[0], bufs[NB - 1], bufs[1 % NB]);
+    if (n0 + 1 < nstage) iter(n0 + 1, bufs[1 % NB], bufs[0], bufs[2 % NB]);
     if constexpr (NB > 2)
-      if (n0 + 2 < nstage) stage_body(n0 + 2, bufs[2 % NB], bufs[1], bufs[3 % NB]);
+      if (n0 + 2 < nstage) iter(n0 + 2, bufs[2 % NB], bufs[1], bufs[3 % NB]);
     if constexpr (NB > 3)
-      if (n0 + 3 < nstage) stage_body(n0 + 3, bufs[3 % NB], bufs[2], bufs[4 % NB]);
+      if (n0 + 3 < nstage) iter(n0 + 3, bufs[3 % NB], bufs[2], bufs[4 % NB]);
   }
+  if (PP && !late) lds_barrier();
 
-  // ---- epilogue: normalise; final output for unsplit sequences, partials otherwise
-  const float inv_l = 1.f / l_run;
+  // ---- epilogue: normalise; final output for unsplit sequences, partials otherwise.  A unit
+  // with no tokens (an empty sequence) has l = 0 and gives out = 0, lse = -inf.
+  const float inv_l = l_run > 0.f ? 1.f / l_run : 0.f;
   const float lse_v = (m_run + log2f(l_run)) * kLn2;
-  if (!valid) return;
-  const int c_wave = half * C::CBW * 32;  // first O column this wave holds
   if (nsplit == 1) {
+    if (!valid) return;
     const size_t orow = (size_t)b * a.rows + row;
     if (h == 0 && half == 0) a.lse[orow] = lse_v;
 #pragma unroll
     for (int k = 0; k < C::CBW; ++k) {
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
-        const int c = c_wave + k * 32 + 8 * g4 + 4 * h;
+        const int c = (half * C::CBW + k) * 32 + 8 * g4 + 4 * h;
         const float o0 = acc[k][4 * g4 + 0] * inv_l, o1 = acc[k][4 * g4 + 1] * inv_l;
         const float o2 = acc[k][4 * g4 + 2] * inv_l, o3 = acc[k][4 * g4 + 3] * inv_l;
         if (a.out_bf16) {
@@ -657,17 +713,32 @@ __global__ __launch_bounds__(NSETS* HB* SPLIT * 64) void decode_kernel(DecodeArg
       }
     }
   } else {
-    const size_t prow = (size_t)unit * a.rows + row;
-    if (h == 0 && half == 0) a.part_lse[prow] = lse_v;
+    // Partials in fragment order: slot block (unit, set, head block) holds 32 heads x DL values
+    // as [column block][piece][lane][value], a piece being 8 (bf16) or 4 (f32) consecutive
+    // accumulator registers, so every store instruction writes 1 KB contiguous.  All lanes
+    // store (those past the set's heads hold finite values the combine ignores).
+    const size_t blk = ((size_t)unit * G + gs) * HB + hb;
+    if (h == 0 && half == 0) a.part_lse[blk * 32 + col] = lse_v;
+    if (a.part_bf16) {
+      __bf16* dst = static_cast<__bf16*>(a.part_out) + blk * (32 * DL);
 #pragma unroll
-    for (int k = 0; k < C::CBW; ++k) {
+      for (int k = 0; k < C::CBW; ++k)
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int c = c_wave + k * 32 + 8 * g4 + 4 * h;
-        float* dst = a.part_out + prow * DL + c;
-        *reinterpret_cast<float4*>(dst) = make_float4(acc[k][4 * g4] * inv_l, acc[k][4 * g4 + 1] * inv_l,
-                                                      acc[k][4 * g4 + 2] * inv_l, acc[k][4 * g4 + 3] * inv_l);
-      }
+        for (int j = 0; j < 2; ++j) {
+          bf16x8_t v;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] = (__bf16)(acc[k][8 * j + e] * inv_l);
+          *reinterpret_cast<bf16x8_t*>(dst + (((half * C::CBW + k) * 2 + j) * 64 + lane) * 8) = v;
+        }
+    } else {
+      float* dst = static_cast<float*>(a.part_out) + blk * (32 * DL);
+#pragma unroll
+      for (int k = 0; k < C::CBW; ++k)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          *reinterpret_cast<float4*>(dst + (((half * C::CBW + k) * 4 + j) * 64 + lane) * 4) =
+              make_float4(acc[k][4 * j] * inv_l, acc[k][4 * j + 1] * inv_l, acc[k][4 * j + 2] * inv_l,
+                          acc[k][4 * j + 3] * inv_l);
     }
   }
 }

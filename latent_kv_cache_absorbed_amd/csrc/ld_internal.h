@@ -36,8 +36,11 @@ struct WsLayout {
   size_t header = 0;       // int32[64]: [0] num_units, [1] chunk
   size_t units = 0;        // Unit[max_units]
   size_t seqs = 0;         // int32[2*B]: (num_splits, first_unit) per sequence
-  size_t part_lse = 0;     // f32[max_units][R]
-  size_t part_out = 0;     // f32[max_units][R][d_v]
+  // Split partials, one slot per (unit, set, 32-head block, head): slots = max_units * G * hblocks * 32.
+  // part_out holds each slot block's 32 x d_v values in MFMA-fragment order (see decode.hip),
+  // bf16 when the output is bf16, else f32.
+  size_t part_lse = 0;     // f32[slots]
+  size_t part_out = 0;     // [slots][d_v]
   size_t total = 0;
 };
 
@@ -57,12 +60,13 @@ struct DecodeArgs {
   const Unit* units;
   const int32_t* seqs;
   float* part_lse;
-  float* part_out;
+  void* part_out;
   int32_t batch, heads, groups, heads_per_set, rows, max_pages, num_pages, page_size;
   int32_t nsets, hblocks;       // sets per work group, 32-head blocks per set
   int32_t wg_per_unit;          // work groups per unit (= groups / nsets)
   int32_t max_units;
   int32_t out_bf16;
+  int32_t part_bf16;            // partials stored as bf16 (else f32)
   int32_t mlra;
   float scale_log2;             // softmax_scale * log2(e)
 };

@@ -93,48 +93,84 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   }
 }
 
-// Merge split partials of every row of every sequence whose split count is not 1.
-// Work group = one sequence and `RPB` rows; one thread per (row, 4 columns).
+// Merge the split partials of every sequence whose split count is not 1.  The partials are in
+// the decode kernel's fragment order: slot block (unit, set, 32-head block) holds 32 heads x d_v
+// values as [column block][piece][lane][value], where a piece is the 8 (bf16) or 4 (f32)
+// consecutive accumulator registers of one lane: register i of lane l holds head l % 32 and
+// column 32 * cb + 8 * (i / 4) + 4 * (l / 32) + i % 4.  One thread merges one piece position
+// over all of the sequence's splits, so every load is a 16-byte piece that its neighbours
+// continue.
 constexpr int kCombineThreads = 256;
 
-__global__ __launch_bounds__(kCombineThreads) void combine_ws_kernel(DecodeArgs a, int d_v, int rows_per_block) {
+__global__ __launch_bounds__(kCombineThreads) void combine_ws_kernel(DecodeArgs a, int d_v) {
   const int b = blockIdx.y;
   int n = a.seqs[2 * b];
   if (n == 1) return;
   const int first = a.seqs[2 * b + 1];
   n = max(0, min(n, a.max_units - first));  // the planner never exceeds the workspace; stay inside it regardless
-  const int c4n = d_v >> 2;
-  const int r0 = blockIdx.x * rows_per_block;
-  for (int idx = threadIdx.x; idx < rows_per_block * c4n; idx += blockDim.x) {
-    const int r = r0 + idx / c4n;
-    if (r >= a.rows) break;
-    const int c = (idx % c4n) * 4;
-    float M = -INFINITY;
-    for (int s = 0; s < n; ++s) M = fmaxf(M, a.part_lse[(size_t)(first + s) * a.rows + r]);
-    float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-    float lse = -INFINITY;
-    if (M != -INFINITY) {
-      float tot = 0.f;
-      for (int s = 0; s < n; ++s) tot += expf(a.part_lse[(size_t)(first + s) * a.rows + r] - M);
-      lse = M + logf(tot);
-      for (int s = 0; s < n; ++s) {
-        const size_t pr = (size_t)(first + s) * a.rows + r;
-        const float w = expf(a.part_lse[pr] - lse);
-        const float4 v = *reinterpret_cast<const float4*>(a.part_out + pr * d_v + c);
-        o.x += w * v.x;
-        o.y += w * v.y;
-        o.z += w * v.z;
-        o.w += w * v.w;
+  const int vals = a.part_bf16 ? 8 : 4;     // values per piece
+  const int jn = 16 / vals;                 // pieces per lane and column block
+  const int cbn = d_v / 32;
+  const int HB = a.hblocks;
+  const int G = a.groups;
+  const int pieces = G * HB * cbn * jn * 64;  // per unit
+  const int p = blockIdx.x * blockDim.x + threadIdx.x;
+  if (p >= pieces) return;
+  const int lane = p & 63;
+  int rest = p >> 6;
+  const int j = rest % jn;
+  rest /= jn;
+  const int cb = rest % cbn;
+  rest /= cbn;
+  const int hb = rest % HB;
+  const int gs = rest / HB;
+  const int head_in_set = hb * 32 + (lane & 31);
+  if (head_in_set >= a.heads_per_set) return;
+  const int h = lane >> 5;
+  const size_t blk_in_unit = (size_t)gs * HB + hb;
+  const size_t blocks_per_unit = (size_t)G * HB;
+  auto lse_of = [&](int s) { return a.part_lse[((first + s) * blocks_per_unit + blk_in_unit) * 32 + (lane & 31)]; };
+
+  float M = -INFINITY;
+  for (int s = 0; s < n; ++s) M = fmaxf(M, lse_of(s));
+  float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float lse = -INFINITY;
+  if (M != -INFINITY) {
+    float tot = 0.f;
+    for (int s = 0; s < n; ++s) tot += expf(lse_of(s) - M);
+    lse = M + logf(tot);
+    const size_t piece_off = ((size_t)(cb * jn + j) * 64 + lane) * vals;
+    for (int s = 0; s < n; ++s) {
+      const float w = expf(lse_of(s) - lse);
+      const size_t off = ((first + s) * blocks_per_unit + blk_in_unit) * (size_t)(32 * d_v) + piece_off;
+      if (a.part_bf16) {
+        typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+        const bf16x8_t v = *reinterpret_cast<const bf16x8_t*>(static_cast<const __bf16*>(a.part_out) + off);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] += w * (float)v[e];
+      } else {
+        const float4 v = *reinterpret_cast<const float4*>(static_cast<const float*>(a.part_out) + off);
+        o[0] += w * v.x;
+        o[1] += w * v.y;
+        o[2] += w * v.z;
+        o[3] += w * v.w;
       }
     }
-    const size_t orow = (size_t)b * a.rows + r;
-    if (c == 0) a.lse[orow] = lse;
+  }
+  const int row = a.mlra ? head_in_set * G + gs : gs * a.heads_per_set + head_in_set;
+  const size_t orow = (size_t)b * a.rows + row;
+  if (cb == 0 && j == 0 && h == 0) a.lse[orow] = lse;
+  // value e of piece j is register i = vals * j + e: column 32 cb + 8 (i / 4) + 4 h + i % 4
+  for (int q = 0; q < vals / 4; ++q) {
+    const int i0 = vals * j + 4 * q;
+    const int c = cb * 32 + 8 * (i0 / 4) + 4 * h;
     if (a.out_bf16) {
       typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
-      bf16x4_t v = {(__bf16)o.x, (__bf16)o.y, (__bf16)o.z, (__bf16)o.w};
+      bf16x4_t v = {(__bf16)o[4 * q], (__bf16)o[4 * q + 1], (__bf16)o[4 * q + 2], (__bf16)o[4 * q + 3]};
       *reinterpret_cast<bf16x4_t*>(static_cast<__bf16*>(a.out) + orow * d_v + c) = v;
     } else {
-      *reinterpret_cast<float4*>(static_cast<float*>(a.out) + orow * d_v + c) = o;
+      *reinterpret_cast<float4*>(static_cast<float*>(a.out) + orow * d_v + c) =
+          make_float4(o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]);
     }
   }
 }
@@ -189,10 +225,9 @@ int launch_plan(const PlanArgs& a, void* stream) {
 
 int launch_combine_ws(const DecodeArgs& a, int32_t d_v, void* stream) {
   if (a.batch == 0 || a.rows == 0) return 0;
-  const int rpb = d_v >= 256 ? 4 : 16;
-  const dim3 grid((a.rows + rpb - 1) / rpb, a.batch);
-  hipLaunchKernelGGL(combine_ws_kernel, grid, dim3(kCombineThreads), 0, static_cast<hipStream_t>(stream), a, d_v,
-                     rpb);
+  const int pieces = a.groups * a.hblocks * (d_v / 32) * (a.part_bf16 ? 2 : 4) * 64;
+  const dim3 grid((pieces + kCombineThreads - 1) / kCombineThreads, a.batch);
+  hipLaunchKernelGGL(combine_ws_kernel, grid, dim3(kCombineThreads), 0, static_cast<hipStream_t>(stream), a, d_v);
   return (int)hipGetLastError();
 }
 
