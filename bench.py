@@ -10,16 +10,22 @@ block table).  Consecutive steps read different copies of the cache (4 copies,
 about 1.2 GB) so the 256 MB Infinity Cache cannot serve a repeat.
 
 Prints one JSON line.  ``value`` is algorithmic KV-cache bytes per second of a
-whole step; ``roofline`` describes the decode kernel alone (timed with HIP
-events on the stream it is launched on); ``cpu_baseline`` is the CPU fp64
-oracle timed on a bounded sample of the same workload.
+whole step; ``roofline`` describes the decode kernel alone (its average
+duration over back-to-back launches, timed with HIP events on the stream it is
+launched on); ``cpu_baseline`` is the CPU fp64 oracle timed on a bounded sample
+of the same workload.
+
+``--summarize-profile TRACE FETCH WRITE`` turns the csv output of three
+rocprofv3 runs of this script (``--kernel-trace --stats``, ``--pmc FETCH_SIZE``
+and ``--pmc WRITE_SIZE``, the last two with ``--calibrate-copy-mib``) into the
+text summaries kept under profiles/.
 """
 from __future__ import annotations
 
 import argparse
+import csv
 import hashlib
 import json
-import math
 import os
 import sys
 import time
@@ -32,6 +38,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
 MFMA_F32_PEAK_TFLOPS = 157.3
 DECODE_SRC = os.path.join(ROOT, "latent_kv_cache_absorbed_amd", "csrc", "decode.hip")
+PROFILES = os.path.join(ROOT, "profiles")
 
 
 def flops_per_token_head(w) -> int:
@@ -48,9 +55,13 @@ def source_sha() -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
+def traffic_path(workload: str) -> str:
+    return os.path.join(PROFILES, f"decode_{workload}_traffic.json")
+
+
 def traffic_from_profile(workload: str):
     """HBM bytes per decode launch from committed rocprofv3 counter summaries, if they match this kernel."""
-    path = os.path.join(ROOT, "profiles", f"decode_{workload}_traffic.json")
+    path = traffic_path(workload)
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -61,7 +72,8 @@ def traffic_from_profile(workload: str):
 
 
 def cpu_baseline(inp, budget_s: float):
-    """Time the oracle as it stands on a bounded sample of sequences (all heads each)."""
+    """Time the oracle as it stands on a bounded sample: whole sequences (all heads), repeated until the
+    budget is spent."""
     import numpy as np
 
     import oracle
@@ -76,19 +88,84 @@ def cpu_baseline(inp, budget_s: float):
     kw = dict(groups=inp.groups, scale=inp.scale, page_size=inp.layout.page_size, v_pool=f64(inp.v_pool),
               rope_pool=f64(inp.rope_pool), scale_pool=f64(inp.scale_pool), d_rope=inp.d_rope)
     B = inp.batch
+    lens = inp.layout.seq_lens.astype(np.int64)
     t0 = time.perf_counter()
     oracle.decode_paged(*args, batches=[0], **kw)
     t1 = time.perf_counter() - t0
     n = int(max(1, min(B, budget_s / max(t1, 1e-3))))
+    batches = list(range(n))
+    reps, toks = 0, 0
     t0 = time.perf_counter()
-    oracle.decode_paged(*args, batches=list(range(n)), **kw)
-    dt = time.perf_counter() - t0
-    per_tok = inp.kv_bytes() / max(1, int(inp.layout.seq_lens.astype(np.int64).sum()))
-    toks = int(inp.layout.seq_lens[:n].astype(np.int64).sum())
+    while True:
+        oracle.decode_paged(*args, batches=batches, **kw)
+        reps += 1
+        toks += int(lens[:n].sum())
+        dt = time.perf_counter() - t0
+        if dt >= min(budget_s, 10.0) or dt * (reps + 1) / reps > 3 * budget_s:
+            break
+    per_tok = inp.kv_bytes() / max(1, int(lens.sum()))
     gbs = per_tok * toks / dt / 1e9
     return {"value": round(gbs, 4), "unit": "GB/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"{n} of {B} sequences x all {inp.heads} heads ({toks} cached tokens), fp64 numpy, "
-                      f"{dt:.1f} s", "seconds": round(dt, 3), "tokens_per_s": round(n / dt, 3)}
+            "sample": f"{n} of {B} sequences x all {inp.heads} heads, {reps} pass(es), {toks} cached tokens, "
+                      f"fp64 numpy, {dt:.1f} s", "seconds": round(dt, 3), "tokens_per_s": round(n * reps / dt, 3)}
+
+
+def _kernel_rows(trace_dir: str):
+    with open(os.path.join(trace_dir, "run_kernel_stats.csv")) as f:
+        return list(csv.DictReader(f))
+
+
+def _counter(dir_: str, name: str):
+    rows = list(csv.DictReader(open(os.path.join(dir_, "run_counter_collection.csv"))))
+    out = {}
+    for r in rows:
+        if r["Counter_Name"] == name:
+            out.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return out
+
+
+def summarize_profile(workload: str, trace_dir: str, fetch_dir: str, write_dir: str, copy_mib: int,
+                      commands: list[str]) -> None:
+    """Write profiles/decode_kernel_<workload>.md and profiles/decode_<workload>_traffic.json."""
+    import numpy as np
+
+    stats = _kernel_rows(trace_dir)
+    fetch = _counter(fetch_dir, "FETCH_SIZE")
+    write = _counter(write_dir, "WRITE_SIZE")
+    copy_kib = copy_mib * 1024
+    dec = lambda d: [v for k, v in d.items() if "decode_kernel" in k][0]  # noqa: E731
+    # calibration: the copy of exactly copy_mib MiB reads and writes copy_kib KiB
+    fcopy = [v for k, vs in fetch.items() if "copyBuffer" in k for v in vs if abs(v - copy_kib) < 0.6 * copy_kib]
+    wcopy = [v for k, vs in write.items() if "copyBuffer" in k for v in vs if abs(v - copy_kib) < 0.6 * copy_kib]
+    fscale = copy_kib / fcopy[-1]
+    wscale = copy_kib / wcopy[-1]
+    f_kib = float(np.median(dec(fetch)))
+    w_kib = float(np.median(dec(write)))
+    hbm = (f_kib * fscale + w_kib * wscale) * 1024
+    t = {"workload": workload, "decode_source_sha": source_sha(), "hbm_bytes_per_launch": int(hbm),
+         "fetch_kib_per_dispatch": f_kib, "write_kib_per_dispatch": w_kib, "fetch_scale": round(fscale, 5),
+         "write_scale": round(wscale, 5), "calibration": f"plain device copy of {copy_mib} MiB",
+         "commands": commands[1:]}
+    with open(traffic_path(workload), "w") as f:
+        json.dump(t, f, indent=1)
+        f.write("\n")
+    lines = [f"# decode_kernel, workload {workload}", "",
+             "Kernel durations (rocprofv3 kernel trace, whole run incl. warm-up):", "",
+             f"    {commands[0]}", "",
+             "| kernel | calls | average us | min us | max us |", "|---|---|---|---|---|"]
+    for r in stats:
+        lines.append(f"| {r['Name'][:90]} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                     f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} |")
+    lines += ["", "HBM traffic of one decode launch (TCC counters, one pass per counter):", ""]
+    lines += [f"    {c}" for c in commands[1:]]
+    lines += ["", f"- FETCH_SIZE {f_kib:.0f} KiB per dispatch; the {copy_mib} MiB copy reads {fcopy[-1]:.0f} KiB "
+                  f"-> scale {fscale:.4f}",
+              f"- WRITE_SIZE {w_kib:.0f} KiB per dispatch; the copy writes {wcopy[-1]:.0f} KiB -> scale {wscale:.4f}",
+              f"- HBM bytes per launch: {hbm / 1e6:.1f} MB (read {f_kib * fscale * 1024 / 1e6:.1f} MB, "
+              f"write {w_kib * wscale * 1024 / 1e6:.1f} MB)",
+              f"- decode source sha256[:16] {source_sha()}", ""]
+    with open(os.path.join(PROFILES, f"decode_kernel_{workload}.md"), "w") as f:
+        f.write("\n".join(lines))
 
 
 def main() -> int:
@@ -103,7 +180,14 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="also run one device copy of this many MiB (counter calibration runs)")
+    ap.add_argument("--summarize-profile", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--profile-commands", nargs=3, default=None, help="the three commands, for the summary")
     args = ap.parse_args()
+
+    if args.summarize_profile:
+        cmds = args.profile_commands or ["(not given)"] * 3
+        summarize_profile(args.workload, *args.summarize_profile, args.calibrate_copy_mib or 512, cmds)
+        return 0
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -148,28 +232,41 @@ def main() -> int:
         decs[i % len(decs)].run()
     torch.cuda.synchronize()
 
+    # ---- the timed steps: plan + decode + combine, K times back to back
     K = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record(stream)
     for i in range(K):
-        d = decs[i % len(decs)]
-        e = ev[i]
-        e[0].record(stream)
-        d.plan()
-        e[1].record(stream)
-        d.decode()
-        e[2].record(stream)
-        d.combine()
-        e[3].record(stream)
+        decs[i % len(decs)].run()
     stop.record(stream)
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(stop)
-    plan_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
-    dec_all = np.array([e[1].elapsed_time(e[2]) for e in ev])
-    comb_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in ev]))
-    dec_ms = float(np.mean(dec_all))
+
+    # ---- per-stage kernel durations: each stage launched K times back to back (the plan only depends
+    # on seq_lens, so one plan serves every decode and combine launch), per-launch average
+    def timed(fn):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(K):
+            fn(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / K
+
+    plan_ms = timed(lambda i: decs[i % len(decs)].plan())
+    dec_ms = timed(lambda i: decs[i % len(decs)].decode())
+    comb_ms = timed(lambda i: decs[i % len(decs)].combine())
+    # single-launch spread of the decode kernel
+    one = []
+    for i in range(min(K, 20)):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        decs[i % len(decs)].decode()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        one.append(e0.elapsed_time(e1))
 
     if args.calibrate_copy_mib:
         n = args.calibrate_copy_mib << 20
@@ -215,8 +312,9 @@ def main() -> int:
         "kv_tokens_per_s": round(float(lens.sum()) / t, 1),
         "hbm_frac_step": round((kv_bytes + q_bytes + out_bytes) / t / 1e9 / HBM_PEAK_GBS, 4),
         "stage_ms": {"plan": round(plan_ms, 5), "decode": round(dec_ms, 5), "combine": round(comb_ms, 5),
-                     "decode_p10": round(float(np.percentile(dec_all, 10)), 5),
-                     "decode_p90": round(float(np.percentile(dec_all, 90)), 5)},
+                     "decode_single_p10": round(float(np.percentile(one, 10)), 5),
+                     "decode_single_p50": round(float(np.percentile(one, 50)), 5),
+                     "decode_single_p90": round(float(np.percentile(one, 90)), 5)},
         "roofline": {"kernel": "decode_kernel", "bound": "hbm", "achieved": round(achieved, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "alg_bytes_per_launch": int(dec_alg_bytes),

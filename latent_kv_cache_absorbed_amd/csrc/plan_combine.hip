@@ -18,11 +18,16 @@ namespace {
 
 __device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
 
+constexpr int kOwnUnits = 8;
+
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   __shared__ long long red[kPlanThreads / 64];
   __shared__ int scan[kPlanThreads];
   __shared__ int s_chunk;
   __shared__ int s_carry;
+  __shared__ int s_nlong;
+  __shared__ int long_b[kPlanThreads], long_n[kPlanThreads], long_first[kPlanThreads], long_L[kPlanThreads],
+      long_ck[kPlanThreads];
   const int tid = threadIdx.x;
   const int page = a.page_size;
 
@@ -68,21 +73,37 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
       __syncthreads();
     }
     const int first = s_carry + scan[tid] - n;
+    auto write_unit = [&](int bb, int s, int f, int LL, int c) {
+      const int u = f + s;
+      if (u < a.max_units) {
+        Unit rec;
+        rec.b = bb;
+        rec.t_begin = s * c;
+        rec.t_end = min(LL, (s + 1) * c);
+        rec.split = s;
+        a.units[u] = rec;
+      }
+    };
+    // each thread writes the first kOwnUnits units of its sequence; the units beyond those (long
+    // sequences split many ways) are written by the whole work group, one such sequence at a time
+    if (tid == 0) s_nlong = 0;
+    __syncthreads();
     if (b < a.batch) {
       a.seqs[2 * b] = n;
       a.seqs[2 * b + 1] = first;
-      for (int s = 0; s < n; ++s) {
-        const int u = first + s;
-        if (u < a.max_units) {
-          Unit rec;
-          rec.b = b;
-          rec.t_begin = s * ck;
-          rec.t_end = min(L, (s + 1) * ck);
-          rec.split = s;
-          a.units[u] = rec;
-        }
+      for (int s = 0; s < n && s < kOwnUnits; ++s) write_unit(b, s, first, L, ck);
+      if (n > kOwnUnits) {
+        const int slot = atomicAdd(&s_nlong, 1);
+        long_b[slot] = b;
+        long_n[slot] = n;
+        long_first[slot] = first;
+        long_L[slot] = L;
+        long_ck[slot] = ck;
       }
     }
+    __syncthreads();
+    for (int i = 0; i < s_nlong; ++i)
+      for (int s = kOwnUnits + tid; s < long_n[i]; s += blockDim.x) write_unit(long_b[i], s, long_first[i], long_L[i], long_ck[i]);
     __syncthreads();
     if (tid == blockDim.x - 1) s_carry += scan[tid];
     __syncthreads();
@@ -97,12 +118,17 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
 // the decode kernel's fragment order: slot block (unit, set, 32-head block) holds 32 heads x d_v
 // values as [column block][piece][lane][value], where a piece is the 8 (bf16) or 4 (f32)
 // consecutive accumulator registers of one lane: register i of lane l holds head l % 32 and
-// column 32 * cb + 8 * (i / 4) + 4 * (l / 32) + i % 4.  One thread merges one piece position
-// over all of the sequence's splits, so every load is a 16-byte piece that its neighbours
-// continue.
+// column 32 * cb + 8 * (i / 4) + 4 * (l / 32) + i % 4.
+// A work group takes 64 consecutive piece positions of one sequence (one 1 KB load per split) and
+// its four waves split the sequence's splits between them; the waves' sums are added in LDS in a
+// fixed order, so the result does not depend on timing.
 constexpr int kCombineThreads = 256;
+constexpr int kCombineWaves = kCombineThreads / 64;
+constexpr int kCombineFewSplits = 8;  // at most this many splits: one wave merges a piece group alone
 
 __global__ __launch_bounds__(kCombineThreads) void combine_ws_kernel(DecodeArgs a, int d_v) {
+  __shared__ float red_m[kCombineWaves][64];
+  __shared__ float red_o[kCombineWaves][8][64];
   const int b = blockIdx.y;
   int n = a.seqs[2 * b];
   if (n == 1) return;
@@ -113,11 +139,10 @@ __global__ __launch_bounds__(kCombineThreads) void combine_ws_kernel(DecodeArgs 
   const int cbn = d_v / 32;
   const int HB = a.hblocks;
   const int G = a.groups;
-  const int pieces = G * HB * cbn * jn * 64;  // per unit
-  const int p = blockIdx.x * blockDim.x + threadIdx.x;
-  if (p >= pieces) return;
-  const int lane = p & 63;
-  int rest = p >> 6;
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  // piece position p = blockIdx.x * 64 + lane (the piece count per unit is a multiple of 64)
+  int rest = blockIdx.x;
   const int j = rest % jn;
   rest /= jn;
   const int cb = rest % cbn;
@@ -125,22 +150,16 @@ __global__ __launch_bounds__(kCombineThreads) void combine_ws_kernel(DecodeArgs 
   const int hb = rest % HB;
   const int gs = rest / HB;
   const int head_in_set = hb * 32 + (lane & 31);
-  if (head_in_set >= a.heads_per_set) return;
   const int h = lane >> 5;
   const size_t blk_in_unit = (size_t)gs * HB + hb;
   const size_t blocks_per_unit = (size_t)G * HB;
   auto lse_of = [&](int s) { return a.part_lse[((first + s) * blocks_per_unit + blk_in_unit) * 32 + (lane & 31)]; };
 
-  float M = -INFINITY;
-  for (int s = 0; s < n; ++s) M = fmaxf(M, lse_of(s));
-  float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  float lse = -INFINITY;
-  if (M != -INFINITY) {
-    float tot = 0.f;
-    for (int s = 0; s < n; ++s) tot += expf(lse_of(s) - M);
-    lse = M + logf(tot);
-    const size_t piece_off = ((size_t)(cb * jn + j) * 64 + lane) * vals;
-    for (int s = 0; s < n; ++s) {
+  const size_t piece_off = ((size_t)(cb * jn + j) * 64 + lane) * vals;
+  // this wave's share (splits s0, s0 + step, ...) of the weighted sum, loads unrolled for overlap
+  auto accumulate = [&](int s0, int step, float lse, float* o) {
+#pragma unroll 8
+    for (int s = s0; s < n; s += step) {
       const float w = expf(lse_of(s) - lse);
       const size_t off = ((first + s) * blocks_per_unit + blk_in_unit) * (size_t)(32 * d_v) + piece_off;
       if (a.part_bf16) {
@@ -155,6 +174,52 @@ __global__ __launch_bounds__(kCombineThreads) void combine_ws_kernel(DecodeArgs 
         o[2] += w * v.z;
         o[3] += w * v.w;
       }
+    }
+  };
+  float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float lse;
+  if (n <= kCombineFewSplits) {
+    // few splits: one wave does the whole piece group, no cross-wave reduction
+    if (wave != 0) return;
+    float M = -INFINITY;
+    for (int s = 0; s < n; ++s) M = fmaxf(M, lse_of(s));
+    float tot = 0.f;
+    if (M != -INFINITY)
+      for (int s = 0; s < n; ++s) tot += expf(lse_of(s) - M);
+    lse = (M == -INFINITY) ? -INFINITY : M + logf(tot);
+    if (M != -INFINITY) accumulate(0, 1, lse, o);
+    if (head_in_set >= a.heads_per_set) return;
+  } else {
+    // combined lse of this lane's head
+    float M = -INFINITY;
+#pragma unroll 4
+    for (int s = wave; s < n; s += kCombineWaves) M = fmaxf(M, lse_of(s));
+    red_m[wave][lane] = M;
+    __syncthreads();
+    M = red_m[0][lane];
+#pragma unroll
+    for (int w = 1; w < kCombineWaves; ++w) M = fmaxf(M, red_m[w][lane]);
+    __syncthreads();
+    float tot = 0.f;
+#pragma unroll 4
+    for (int s = wave; s < n; s += kCombineWaves) tot += expf(lse_of(s) - M);
+    red_m[wave][lane] = tot;
+    __syncthreads();
+    tot = 0.f;
+#pragma unroll
+    for (int w = 0; w < kCombineWaves; ++w) tot += red_m[w][lane];
+    lse = M + logf(tot);  // n > kCombineFewSplits >= 1 non-empty splits: M is finite
+    accumulate(wave, kCombineWaves, lse, o);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) red_o[wave][e][lane] = o[e];
+    __syncthreads();
+    if (wave != 0 || head_in_set >= a.heads_per_set) return;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float t = red_o[0][e][lane];
+#pragma unroll
+      for (int w = 1; w < kCombineWaves; ++w) t += red_o[w][e][lane];
+      o[e] = t;
     }
   }
   const int row = a.mlra ? head_in_set * G + gs : gs * a.heads_per_set + head_in_set;
@@ -226,7 +291,7 @@ int launch_plan(const PlanArgs& a, void* stream) {
 int launch_combine_ws(const DecodeArgs& a, int32_t d_v, void* stream) {
   if (a.batch == 0 || a.rows == 0) return 0;
   const int pieces = a.groups * a.hblocks * (d_v / 32) * (a.part_bf16 ? 2 : 4) * 64;
-  const dim3 grid((pieces + kCombineThreads - 1) / kCombineThreads, a.batch);
+  const dim3 grid(pieces / 64, a.batch);
   hipLaunchKernelGGL(combine_ws_kernel, grid, dim3(kCombineThreads), 0, static_cast<hipStream_t>(stream), a, d_v);
   return (int)hipGetLastError();
 }

@@ -138,3 +138,15 @@ def test_split_combine_standalone():
             continue
         assert np.max(np.abs(o[i] - eo)) <= 1e-5 * max(1.0, np.max(np.abs(eo)))
         assert abs(l[i] - el) <= 1e-5 * max(1.0, abs(el))
+
+
+# --- one long sequence split many ways (planner units written cooperatively, multi-wave combine)
+def test_mla_bf16_one_long_sequence_many_splits():
+    inp = synth.make_inputs("mla", 1, 128, 1, 512, 64, [40000], scale=1 / math.sqrt(192), seed=22)
+    _check(inp)
+
+
+@pytest.mark.parametrize("splits", [9, 40])
+def test_mla_bf16_forced_many_splits(splits):
+    inp = synth.make_inputs("mla", 3, 128, 1, 512, 64, [5000, 64, 2600], scale=1 / math.sqrt(192), seed=23)
+    _check(inp, num_splits=splits)
