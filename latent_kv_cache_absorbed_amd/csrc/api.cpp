@@ -2,6 +2,7 @@
 // planner, and the launch sequence plan -> decode -> combine.  See include/latent_decode.h.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -47,12 +48,30 @@ WsLayout ws_layout(const ld_problem& p, int num_cus) {
   w.units = off;
   off = round256(off + (size_t)w.max_units * sizeof(Unit));
   w.seqs = off;
-  off = round256(off + (size_t)p.batch * 2 * sizeof(int32_t));
+  off = round256(off + (size_t)p.batch * 4 * sizeof(int32_t));
   const size_t slots = (size_t)w.max_units * p.num_groups * launch_shape(p).hblocks * 32;
   w.part_lse = off;
   off = round256(off + slots * sizeof(float));
   w.part_out = off;
   off = round256(off + slots * w.d_v * (p.out_dtype == LD_BF16 ? 2 : 4));
+  // combine tasks: a sequence with n > 1 splits is merged in ceil(n / kCombineChunk) chunks (an empty
+  // one in one task), so there are at most max_units / kCombineChunk + B of them
+  w.max_tasks = p.num_splits > 0 ? p.batch * ((p.num_splits + kCombineChunk - 1) / kCombineChunk)
+                                 : (w.max_units + kCombineChunk - 1) / kCombineChunk + p.batch;
+  const size_t vals = p.out_dtype == LD_BF16 ? 8 : 4;   // values per piece
+  const size_t pieces = (size_t)p.num_groups * launch_shape(p).hblocks * (w.d_v / 32) * (16 / vals) * 64;
+  w.xblocks = (int32_t)(pieces / 256);
+  w.tasks = off;
+  off = round256(off + (size_t)w.max_tasks * 2 * sizeof(int32_t));
+  // a sequence merged in more than one chunk has more than kCombineChunk units
+  w.max_multi = p.num_splits > 0 ? (p.num_splits > kCombineChunk ? p.batch : 0)
+                                 : std::min<int32_t>(p.batch, w.max_units / (kCombineChunk + 1));
+  w.multi = off;
+  off = round256(off + (size_t)(w.max_multi > 0 ? w.max_multi : 1) * sizeof(int32_t));
+  w.l2_out = off;
+  off = round256(off + (size_t)w.max_tasks * pieces * vals * sizeof(float));
+  w.l2_lse = off;
+  off = round256(off + (size_t)w.max_tasks * pieces * sizeof(float));
   w.total = off;
   return w;
 }
@@ -251,6 +270,13 @@ DecodeArgs decode_args(const ld_problem* p, const WsLayout& w, void* workspace) 
   a.seqs = reinterpret_cast<const int32_t*>(ws + w.seqs);
   a.part_lse = reinterpret_cast<float*>(ws + w.part_lse);
   a.part_out = ws + w.part_out;
+  a.tasks = reinterpret_cast<const int32_t*>(ws + w.tasks);
+  a.multi = reinterpret_cast<const int32_t*>(ws + w.multi);
+  a.l2_out = reinterpret_cast<float*>(ws + w.l2_out);
+  a.l2_lse = reinterpret_cast<float*>(ws + w.l2_lse);
+  a.max_tasks = w.max_tasks;
+  a.max_multi = w.max_multi;
+  a.xblocks = w.xblocks;
   a.batch = p->batch;
   a.heads = p->num_q_heads;
   a.groups = p->num_groups;
@@ -289,6 +315,10 @@ int32_t ld_plan(const ld_problem* p, const int32_t* seq_lens, void* workspace, s
   pa.header = reinterpret_cast<int32_t*>(ws + w.header);
   pa.units = reinterpret_cast<Unit*>(ws + w.units);
   pa.seqs = reinterpret_cast<int32_t*>(ws + w.seqs);
+  pa.tasks = reinterpret_cast<int32_t*>(ws + w.tasks);
+  pa.multi = reinterpret_cast<int32_t*>(ws + w.multi);
+  pa.max_tasks = w.max_tasks;
+  pa.max_multi = w.max_multi;
   pa.batch = p->batch;
   pa.capacity = p->max_pages_per_seq * p->page_size;
   pa.page_size = p->page_size;

@@ -279,7 +279,7 @@ __global__ __launch_bounds__(NSETS* HB* SPLIT * 64) void decode_kernel(DecodeArg
   const int b = u.b;
   const int t_begin = u.t_begin;
   const int t_end = u.t_end;
-  const int nsplit = a.seqs[2 * b];
+  const int nsplit = a.seqs[4 * b];
 
   const int set0 = sb * NSETS;
   const int G = a.groups;

@@ -19,6 +19,7 @@ enum Kind : int {
 constexpr int kTile = 32;            // tokens per MFMA tile (one 32-row block)
 constexpr int kWaveSize = 64;
 constexpr int kPlanThreads = 1024;
+constexpr int kCombineChunk = 16;     // splits merged by one combine task
 
 // Work unit record written by the planner: one (sequence, token chunk).
 struct alignas(16) Unit {
@@ -31,11 +32,18 @@ struct alignas(16) Unit {
 // Workspace layout (byte offsets from the workspace base, each 256-aligned).
 struct WsLayout {
   int32_t max_units = 0;
+  int32_t max_tasks = 0;   // bound on combine tasks
+  int32_t max_multi = 0;   // bound on sequences with more than one combine task
+  int32_t xblocks = 0;     // work groups per combine task (256 piece positions each)
   int32_t rows = 0;        // R: output rows per sequence
   int32_t d_v = 0;
   size_t header = 0;       // int32[64]: [0] num_units, [1] chunk
   size_t units = 0;        // Unit[max_units]
-  size_t seqs = 0;         // int32[2*B]: (num_splits, first_unit) per sequence
+  size_t seqs = 0;         // int32[4*B]: (num_splits, first_unit, first_task, num_tasks) per sequence
+  size_t tasks = 0;        // int32[2*max_tasks]: (sequence, chunk) combine tasks
+  size_t multi = 0;        // int32[max_multi]: sequences merged in more than one chunk
+  size_t l2_out = 0;       // f32[max_tasks][pieces][values]: chunk results of multi-chunk sequences
+  size_t l2_lse = 0;       // f32[max_tasks][pieces]: their lse, per piece lane
   // Split partials, one slot per (unit, set, 32-head block, head): slots = max_units * G * hblocks * 32.
   // part_out holds each slot block's 32 x d_v values in MFMA-fragment order (see decode.hip),
   // bf16 when the output is bf16, else f32.
@@ -61,6 +69,11 @@ struct DecodeArgs {
   const int32_t* seqs;
   float* part_lse;
   void* part_out;
+  const int32_t* tasks;
+  const int32_t* multi;
+  float* l2_out;
+  float* l2_lse;
+  int32_t max_tasks, max_multi, xblocks;
   int32_t batch, heads, groups, heads_per_set, rows, max_pages, num_pages, page_size;
   int32_t nsets, hblocks;       // sets per work group, 32-head blocks per set
   int32_t wg_per_unit;          // work groups per unit (= groups / nsets)
@@ -76,6 +89,10 @@ struct PlanArgs {
   int32_t* header;
   Unit* units;
   int32_t* seqs;
+  int32_t* tasks;
+  int32_t* multi;
+  int32_t max_tasks;
+  int32_t max_multi;
   int32_t batch;
   int32_t capacity;       // max_pages_per_seq * page_size
   int32_t page_size;

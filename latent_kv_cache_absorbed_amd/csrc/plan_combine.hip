@@ -23,8 +23,12 @@ constexpr int kOwnUnits = 8;
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   __shared__ long long red[kPlanThreads / 64];
   __shared__ int scan[kPlanThreads];
+  __shared__ int scan2[kPlanThreads];
+  __shared__ int scan3[kPlanThreads];
   __shared__ int s_chunk;
   __shared__ int s_carry;
+  __shared__ int s_carry2;
+  __shared__ int s_carry3;
   __shared__ int s_nlong;
   __shared__ int long_b[kPlanThreads], long_n[kPlanThreads], long_first[kPlanThreads], long_L[kPlanThreads],
       long_ck[kPlanThreads];
@@ -48,6 +52,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     }
     s_chunk = chunk;
     s_carry = 0;
+    s_carry2 = 0;
+    s_carry3 = 0;
   }
   __syncthreads();
   const int chunk = s_chunk;
@@ -64,15 +70,27 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
       }
       n = (L + ck - 1) / ck;
     }
+    // combine tasks of this sequence: none for one split (the decode kernel writes the output),
+    // one for an empty sequence (it writes zeros), else one per chunk of kCombineChunk splits
+    const int nc = (b >= a.batch || n == 1) ? 0 : (n == 0 ? 1 : (n + kCombineChunk - 1) / kCombineChunk);
+    const int mc = nc > 1 ? 1 : 0;
     scan[tid] = n;
+    scan2[tid] = nc;
+    scan3[tid] = mc;
     __syncthreads();
     for (int off = 1; off < (int)blockDim.x; off <<= 1) {
       const int v = tid >= off ? scan[tid - off] : 0;
+      const int v2 = tid >= off ? scan2[tid - off] : 0;
+      const int v3 = tid >= off ? scan3[tid - off] : 0;
       __syncthreads();
       scan[tid] += v;
+      scan2[tid] += v2;
+      scan3[tid] += v3;
       __syncthreads();
     }
     const int first = s_carry + scan[tid] - n;
+    const int ftask = s_carry2 + scan2[tid] - nc;
+    const int mi = s_carry3 + scan3[tid] - mc;
     auto write_unit = [&](int bb, int s, int f, int LL, int c) {
       const int u = f + s;
       if (u < a.max_units) {
@@ -89,8 +107,16 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     if (tid == 0) s_nlong = 0;
     __syncthreads();
     if (b < a.batch) {
-      a.seqs[2 * b] = n;
-      a.seqs[2 * b + 1] = first;
+      a.seqs[4 * b] = n;
+      a.seqs[4 * b + 1] = first;
+      a.seqs[4 * b + 2] = ftask;
+      a.seqs[4 * b + 3] = nc;
+      for (int c = 0; c < nc; ++c)
+        if (ftask + c < a.max_tasks) {
+          a.tasks[2 * (ftask + c)] = b;
+          a.tasks[2 * (ftask + c) + 1] = c;
+        }
+      if (mc && mi < a.max_multi) a.multi[mi] = b;
       for (int s = 0; s < n && s < kOwnUnits; ++s) write_unit(b, s, first, L, ck);
       if (n > kOwnUnits) {
         const int slot = atomicAdd(&s_nlong, 1);
@@ -105,12 +131,18 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     for (int i = 0; i < s_nlong; ++i)
       for (int s = kOwnUnits + tid; s < long_n[i]; s += blockDim.x) write_unit(long_b[i], s, long_first[i], long_L[i], long_ck[i]);
     __syncthreads();
-    if (tid == blockDim.x - 1) s_carry += scan[tid];
+    if (tid == blockDim.x - 1) {
+      s_carry += scan[tid];
+      s_carry2 += scan2[tid];
+      s_carry3 += scan3[tid];
+    }
     __syncthreads();
   }
   if (tid == 0) {
     a.header[0] = min(s_carry, a.max_units);
     a.header[1] = chunk;
+    a.header[2] = min(s_carry2, a.max_tasks);
+    a.header[3] = min(s_carry3, a.max_multi);
   }
 }
 
@@ -119,124 +151,178 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
 // values as [column block][piece][lane][value], where a piece is the 8 (bf16) or 4 (f32)
 // consecutive accumulator registers of one lane: register i of lane l holds head l % 32 and
 // column 32 * cb + 8 * (i / 4) + 4 * (l / 32) + i % 4.
-// A work group takes 64 consecutive piece positions of one sequence (one 1 KB load per split) and
-// its four waves split the sequence's splits between them; the waves' sums are added in LDS in a
-// fixed order, so the result does not depend on timing.
+//
+// A combine task is (sequence, chunk of at most kCombineChunk splits).  Work group (x, t) takes
+// task t and 256 piece positions: one 64-lane piece group per wave, one 1 KB load per split, all
+// of a chunk's loads issued together.  A sequence merged in one chunk is finished there; the
+// chunk results of longer ones (f32, same piece order, with their lse) are merged in chunk order
+// by combine_chunks_kernel, launched after it.
 constexpr int kCombineThreads = 256;
-constexpr int kCombineWaves = kCombineThreads / 64;
-constexpr int kCombineFewSplits = 8;  // at most this many splits: one wave merges a piece group alone
 
-__global__ __launch_bounds__(kCombineThreads) void combine_ws_kernel(DecodeArgs a, int d_v) {
-  __shared__ float red_m[kCombineWaves][64];
-  __shared__ float red_o[kCombineWaves][8][64];
-  const int b = blockIdx.y;
-  int n = a.seqs[2 * b];
-  if (n == 1) return;
-  const int first = a.seqs[2 * b + 1];
-  n = max(0, min(n, a.max_units - first));  // the planner never exceeds the workspace; stay inside it regardless
-  const int vals = a.part_bf16 ? 8 : 4;     // values per piece
-  const int jn = 16 / vals;                 // pieces per lane and column block
+struct PieceGroup {
+  int j, cb, hb, gs, lane, h, head_in_set;
+  size_t blk_in_unit, blocks_per_unit, piece_off, pieces;
+};
+
+__device__ __forceinline__ PieceGroup piece_group(const DecodeArgs& a, int d_v, int pg) {
+  PieceGroup p;
+  const int vals = a.part_bf16 ? 8 : 4;
+  const int jn = 16 / vals;
   const int cbn = d_v / 32;
-  const int HB = a.hblocks;
-  const int G = a.groups;
-  const int wave = threadIdx.x >> 6;
-  const int lane = threadIdx.x & 63;
-  // piece position p = blockIdx.x * 64 + lane (the piece count per unit is a multiple of 64)
-  int rest = blockIdx.x;
-  const int j = rest % jn;
+  int rest = pg;                       // pg = ((gs * HB + hb) * cbn + cb) * jn + j
+  p.j = rest % jn;
   rest /= jn;
-  const int cb = rest % cbn;
+  p.cb = rest % cbn;
   rest /= cbn;
-  const int hb = rest % HB;
-  const int gs = rest / HB;
-  const int head_in_set = hb * 32 + (lane & 31);
-  const int h = lane >> 5;
-  const size_t blk_in_unit = (size_t)gs * HB + hb;
-  const size_t blocks_per_unit = (size_t)G * HB;
-  auto lse_of = [&](int s) { return a.part_lse[((first + s) * blocks_per_unit + blk_in_unit) * 32 + (lane & 31)]; };
+  p.hb = rest % a.hblocks;
+  p.gs = rest / a.hblocks;
+  p.lane = threadIdx.x & 63;
+  p.h = p.lane >> 5;
+  p.head_in_set = p.hb * 32 + (p.lane & 31);
+  p.blk_in_unit = (size_t)p.gs * a.hblocks + p.hb;
+  p.blocks_per_unit = (size_t)a.groups * a.hblocks;
+  p.piece_off = ((size_t)(p.cb * jn + p.j) * 64 + p.lane) * vals;
+  p.pieces = (size_t)a.xblocks * 256;
+  return p;
+}
 
-  const size_t piece_off = ((size_t)(cb * jn + j) * 64 + lane) * vals;
-  // this wave's share (splits s0, s0 + step, ...) of the weighted sum, loads unrolled for overlap
-  auto accumulate = [&](int s0, int step, float lse, float* o) {
-#pragma unroll 8
-    for (int s = s0; s < n; s += step) {
-      const float w = expf(lse_of(s) - lse);
-      const size_t off = ((first + s) * blocks_per_unit + blk_in_unit) * (size_t)(32 * d_v) + piece_off;
-      if (a.part_bf16) {
-        typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-        const bf16x8_t v = *reinterpret_cast<const bf16x8_t*>(static_cast<const __bf16*>(a.part_out) + off);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) o[e] += w * (float)v[e];
-      } else {
-        const float4 v = *reinterpret_cast<const float4*>(static_cast<const float*>(a.part_out) + off);
-        o[0] += w * v.x;
-        o[1] += w * v.y;
-        o[2] += w * v.z;
-        o[3] += w * v.w;
-      }
-    }
-  };
-  float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  float lse;
-  if (n <= kCombineFewSplits) {
-    // few splits: one wave does the whole piece group, no cross-wave reduction
-    if (wave != 0) return;
-    float M = -INFINITY;
-    for (int s = 0; s < n; ++s) M = fmaxf(M, lse_of(s));
-    float tot = 0.f;
-    if (M != -INFINITY)
-      for (int s = 0; s < n; ++s) tot += expf(lse_of(s) - M);
-    lse = (M == -INFINITY) ? -INFINITY : M + logf(tot);
-    if (M != -INFINITY) accumulate(0, 1, lse, o);
-    if (head_in_set >= a.heads_per_set) return;
-  } else {
-    // combined lse of this lane's head
-    float M = -INFINITY;
-#pragma unroll 4
-    for (int s = wave; s < n; s += kCombineWaves) M = fmaxf(M, lse_of(s));
-    red_m[wave][lane] = M;
-    __syncthreads();
-    M = red_m[0][lane];
-#pragma unroll
-    for (int w = 1; w < kCombineWaves; ++w) M = fmaxf(M, red_m[w][lane]);
-    __syncthreads();
-    float tot = 0.f;
-#pragma unroll 4
-    for (int s = wave; s < n; s += kCombineWaves) tot += expf(lse_of(s) - M);
-    red_m[wave][lane] = tot;
-    __syncthreads();
-    tot = 0.f;
-#pragma unroll
-    for (int w = 0; w < kCombineWaves; ++w) tot += red_m[w][lane];
-    lse = M + logf(tot);  // n > kCombineFewSplits >= 1 non-empty splits: M is finite
-    accumulate(wave, kCombineWaves, lse, o);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) red_o[wave][e][lane] = o[e];
-    __syncthreads();
-    if (wave != 0 || head_in_set >= a.heads_per_set) return;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      float t = red_o[0][e][lane];
-#pragma unroll
-      for (int w = 1; w < kCombineWaves; ++w) t += red_o[w][e][lane];
-      o[e] = t;
-    }
-  }
-  const int row = a.mlra ? head_in_set * G + gs : gs * a.heads_per_set + head_in_set;
+// out and lse of one piece position (lane) of sequence b
+__device__ __forceinline__ void write_piece(const DecodeArgs& a, int d_v, const PieceGroup& p, int b,
+                                            const float* o, float lse) {
+  if (p.head_in_set >= a.heads_per_set) return;
+  const int vals = a.part_bf16 ? 8 : 4;
+  const int row = a.mlra ? p.head_in_set * a.groups + p.gs : p.gs * a.heads_per_set + p.head_in_set;
   const size_t orow = (size_t)b * a.rows + row;
-  if (cb == 0 && j == 0 && h == 0) a.lse[orow] = lse;
+  if (p.cb == 0 && p.j == 0 && p.h == 0) a.lse[orow] = lse;
   // value e of piece j is register i = vals * j + e: column 32 cb + 8 (i / 4) + 4 h + i % 4
   for (int q = 0; q < vals / 4; ++q) {
-    const int i0 = vals * j + 4 * q;
-    const int c = cb * 32 + 8 * (i0 / 4) + 4 * h;
+    const int i0 = vals * p.j + 4 * q;
+    const int col = p.cb * 32 + 8 * (i0 / 4) + 4 * p.h;
     if (a.out_bf16) {
       typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
       bf16x4_t v = {(__bf16)o[4 * q], (__bf16)o[4 * q + 1], (__bf16)o[4 * q + 2], (__bf16)o[4 * q + 3]};
-      *reinterpret_cast<bf16x4_t*>(static_cast<__bf16*>(a.out) + orow * d_v + c) = v;
+      *reinterpret_cast<bf16x4_t*>(static_cast<__bf16*>(a.out) + orow * d_v + col) = v;
     } else {
-      *reinterpret_cast<float4*>(static_cast<float*>(a.out) + orow * d_v + c) =
+      *reinterpret_cast<float4*>(static_cast<float*>(a.out) + orow * d_v + col) =
           make_float4(o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]);
     }
+  }
+}
+
+// Online merge of (lse, normalised piece) pairs in batches of kBatch: the loads of a batch are
+// issued together (indexes past the last pair repeat it and get weight 0), then the running max,
+// sum and weighted values are updated.  Pairs are taken in index order.
+constexpr int kBatch = 8;
+
+struct Merge {
+  float M = -INFINITY, tot = 0.f, o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  __device__ __forceinline__ void add(const float* ls, const float (*v)[8], int valid, int vals) {
+    float bm = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k)
+      if (k < valid) bm = fmaxf(bm, ls[k]);
+    const float Mn = fmaxf(M, bm);
+    if (Mn == -INFINITY) return;
+    const float r = (M == -INFINITY) ? 0.f : expf(M - Mn);
+    tot *= r;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] *= r;
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      const float w = k < valid ? expf(ls[k] - Mn) : 0.f;
+      tot += w;
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (e < vals) o[e] += w * v[k][e];
+    }
+    M = Mn;
+  }
+  // normalised output and lse (0 and -inf when every lse was -inf)
+  __device__ __forceinline__ float finish() {
+    if (M == -INFINITY) return -INFINITY;
+    const float inv = 1.f / tot;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] *= inv;
+    return M + logf(tot);
+  }
+};
+
+__global__ __launch_bounds__(kCombineThreads) void combine_ws_kernel(DecodeArgs a, int d_v) {
+  const int t = blockIdx.y;
+  if (t >= a.header[2]) return;
+  const int b = a.tasks[2 * t];
+  const int c = a.tasks[2 * t + 1];
+  const int first = a.seqs[4 * b + 1];
+  const int n = max(0, min(a.seqs[4 * b], a.max_units - first));
+  const int ftask = a.seqs[4 * b + 2];
+  const int nc = a.seqs[4 * b + 3];
+  const int pg = 4 * blockIdx.x + (threadIdx.x >> 6);
+  const PieceGroup p = piece_group(a, d_v, pg);
+  const int vals = a.part_bf16 ? 8 : 4;
+  const int s_lo = c * kCombineChunk;
+  const int cnt = max(0, min(n - s_lo, kCombineChunk));  // splits of this chunk
+  Merge m;
+  for (int k0 = 0; k0 < cnt; k0 += kBatch) {
+    float ls[kBatch], v[kBatch][8];
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      const size_t s = first + s_lo + min(k0 + k, cnt - 1);
+      ls[k] = a.part_lse[(s * p.blocks_per_unit + p.blk_in_unit) * 32 + (p.lane & 31)];
+      const size_t off = (s * p.blocks_per_unit + p.blk_in_unit) * (size_t)(32 * d_v) + p.piece_off;
+      if (a.part_bf16) {
+        typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+        const bf16x8_t x = *reinterpret_cast<const bf16x8_t*>(static_cast<const __bf16*>(a.part_out) + off);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[k][e] = (float)x[e];
+      } else {
+        const float4 x = *reinterpret_cast<const float4*>(static_cast<const float*>(a.part_out) + off);
+        v[k][0] = x.x, v[k][1] = x.y, v[k][2] = x.z, v[k][3] = x.w;
+        v[k][4] = v[k][5] = v[k][6] = v[k][7] = 0.f;
+      }
+    }
+    m.add(ls, v, cnt - k0, vals);
+  }
+  if (nc <= 1) {
+    const float lse = m.finish();
+    write_piece(a, d_v, p, b, m.o, lse);
+    return;
+  }
+  // a chunk of a longer sequence: its merged result, for combine_chunks_kernel
+  const float lse = m.finish();
+  const size_t lo = (size_t)(ftask + c) * p.pieces + (size_t)pg * 64 + p.lane;
+  float4* dst = reinterpret_cast<float4*>(a.l2_out + lo * vals);
+  dst[0] = make_float4(m.o[0], m.o[1], m.o[2], m.o[3]);
+  if (vals == 8) dst[1] = make_float4(m.o[4], m.o[5], m.o[6], m.o[7]);
+  a.l2_lse[lo] = lse;
+}
+
+// Merge the chunk results of the sequences combined in more than one chunk, in chunk order.  The
+// grid's second dimension strides over those sequences.
+__global__ __launch_bounds__(kCombineThreads) void combine_chunks_kernel(DecodeArgs a, int d_v) {
+  const int pg = 4 * blockIdx.x + (threadIdx.x >> 6);
+  const PieceGroup p = piece_group(a, d_v, pg);
+  const int vals = a.part_bf16 ? 8 : 4;
+  for (int i = blockIdx.y; i < a.header[3]; i += gridDim.y) {
+    const int b = a.multi[i];
+    const int ftask = a.seqs[4 * b + 2];
+    const int nc = a.seqs[4 * b + 3];
+    Merge m;
+    for (int q0 = 0; q0 < nc; q0 += kBatch) {
+      float ls[kBatch], v[kBatch][8];
+#pragma unroll
+      for (int k = 0; k < kBatch; ++k) {
+        const size_t lo = (size_t)(ftask + min(q0 + k, nc - 1)) * p.pieces + (size_t)pg * 64 + p.lane;
+        ls[k] = a.l2_lse[lo];
+        const float4* src = reinterpret_cast<const float4*>(a.l2_out + lo * vals);
+        const float4 x0 = src[0];
+        const float4 x1 = vals == 8 ? src[1] : make_float4(0.f, 0.f, 0.f, 0.f);
+        v[k][0] = x0.x, v[k][1] = x0.y, v[k][2] = x0.z, v[k][3] = x0.w;
+        v[k][4] = x1.x, v[k][5] = x1.y, v[k][6] = x1.z, v[k][7] = x1.w;
+      }
+      m.add(ls, v, nc - q0, vals);
+    }
+    const float lse = m.finish();
+    write_piece(a, d_v, p, b, m.o, lse);
   }
 }
 
@@ -290,9 +376,13 @@ int launch_plan(const PlanArgs& a, void* stream) {
 
 int launch_combine_ws(const DecodeArgs& a, int32_t d_v, void* stream) {
   if (a.batch == 0 || a.rows == 0) return 0;
-  const int pieces = a.groups * a.hblocks * (d_v / 32) * (a.part_bf16 ? 2 : 4) * 64;
-  const dim3 grid(pieces / 64, a.batch);
-  hipLaunchKernelGGL(combine_ws_kernel, grid, dim3(kCombineThreads), 0, static_cast<hipStream_t>(stream), a, d_v);
+  hipLaunchKernelGGL(combine_ws_kernel, dim3(a.xblocks, a.max_tasks), dim3(kCombineThreads), 0,
+                     static_cast<hipStream_t>(stream), a, d_v);
+  int r = (int)hipGetLastError();
+  if (r != 0 || a.max_multi == 0) return r;
+  const int ys = a.max_multi < 2 ? a.max_multi : 2;  // sequences strided over by the grid
+  hipLaunchKernelGGL(combine_chunks_kernel, dim3(a.xblocks, ys), dim3(kCombineThreads), 0,
+                     static_cast<hipStream_t>(stream), a, d_v);
   return (int)hipGetLastError();
 }
 
