@@ -119,7 +119,8 @@ typedef struct ld_problem {
   int32_t out_dtype;         /* ld_dtype of out: F32 or BF16 */
   float softmax_scale;       /* multiplies q.k; positive and finite (else LD_ERR_BAD_SHAPE);
                                 lse is reported in this scaled domain */
-  int32_t num_splits;        /* 0: the planner splits long sequences over CUs; n >= 1: at most n splits */
+  int32_t num_splits;        /* 0: the planner splits long sequences over CUs; n >= 1: at most n splits,
+                                except that no split spans more than 512 pages */
 } ld_problem;
 
 /* Device pointers of the paged cache (see the layouts above). */
@@ -188,7 +189,7 @@ int32_t ld_validate_metadata(const ld_problem* p, const int32_t* block_table_hos
 /* Host copy of the split-KV planner ld_latent_decode runs on the device, for
  * tests and for callers that plan on the host.  Given the problem, host
  * seq_lens and the number of compute units, writes the chunk length (tokens,
- * a multiple of page_size) and, for every sequence, its split count and the
+ * a multiple of page_size, at most 512 pages) and, for every sequence, its split count and the
  * index of its first work unit.  Returns the number of work units via
  * *num_units.  splits_out and first_unit_out are int32 [batch]. */
 int32_t ld_plan_host(const ld_problem* p, const int32_t* seq_lens_host, int32_t num_cus, int32_t* chunk_out,

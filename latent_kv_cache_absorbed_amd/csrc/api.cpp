@@ -90,12 +90,16 @@ int32_t target_units_for(const ld_problem& p, int32_t num_cus) {
   return t < 1 ? 1 : t;
 }
 
+// A unit spans at most kUnitPages pages, so a sequence has at most ceil(max_pages / kUnitPages)
+// units of the longest length; auto: at most target + B units of the computed chunk on top.
 int32_t max_units_for(const ld_problem& p, int32_t num_cus) {
-  if (p.num_splits > 0) {
-    const long long m = (long long)p.batch * p.num_splits;
-    return (int32_t)(m > (1 << 30) ? (1 << 30) : m);
-  }
-  return target_units_for(p, num_cus) + p.batch;
+  const long long longest = (p.max_pages_per_seq + kUnitPages - 1) / kUnitPages;
+  long long m;
+  if (p.num_splits > 0)
+    m = (long long)p.batch * (p.num_splits > longest ? p.num_splits : longest);
+  else
+    m = target_units_for(p, num_cus) + (long long)p.batch * longest;
+  return (int32_t)(m > (1 << 30) ? (1 << 30) : m);
 }
 
 }  // namespace ld
@@ -195,6 +199,7 @@ int32_t ld_plan_host(const ld_problem* p, const int32_t* seq_lens_host, int32_t 
     const long long per = (total + target - 1) / target;
     chunk = (per + page - 1) / page * page;
     if (chunk < page) chunk = page;
+    if (chunk > (long long)kUnitPages * page) chunk = (long long)kUnitPages * page;
   }
   long long units = 0;
   for (int b = 0; b < p->batch; ++b) {
@@ -204,6 +209,7 @@ int32_t ld_plan_host(const ld_problem* p, const int32_t* seq_lens_host, int32_t 
       const long long per = (L + p->num_splits - 1) / p->num_splits;
       ck = (per + page - 1) / page * page;
       if (ck < page) ck = page;
+      if (ck > (long long)kUnitPages * page) ck = (long long)kUnitPages * page;
     }
     const long long n = (L + ck - 1) / ck;
     splits_out[b] = (int32_t)n;

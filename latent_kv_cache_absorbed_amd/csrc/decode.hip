@@ -47,7 +47,6 @@ typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
 enum KvT : int { KV_F32 = 0, KV_BF16 = 1, KV_FP8 = 2 };
 
 constexpr float kLn2 = 0.69314718055994530942f;
-constexpr int kPageCap = 512;  // block-table entries of a unit staged in LDS
 // The running max is raised only when a stage's max exceeds it by more than this (log2 units),
 // so O is rescaled rarely; scores then stay <= 2^8 above the stale max, far from overflow.
 constexpr float kRescaleSlack = 8.f;
@@ -197,10 +196,10 @@ struct Cfg {
   static constexpr int BUF_AL = (BUF + 127) / 128 * 128;
   static constexpr int EXCH = (SPLIT == 2) ? WAVES * 16 * 64 * 4 : 16;   // partial-score exchange
   // stage buffers: as many as fit (up to 4); the fp8 path stages through registers and keeps two
-  static constexpr int NB_FIT = (160 * 1024 - EXCH - 4 * kPageCap) / BUF_AL;
+  static constexpr int NB_FIT = (160 * 1024 - EXCH - 4 * kUnitPages) / BUF_AL;
   static constexpr int NBUF = (KV == KV_FP8) ? 2 : cmin(NB_FIT, 4);
   static constexpr int LDS_TOTAL =
-      2 * BUF_AL + (NBUF > 2 ? BUF_AL : 128) + (NBUF > 3 ? BUF_AL : 128) + EXCH + 4 * kPageCap;
+      2 * BUF_AL + (NBUF > 2 ? BUF_AL : 128) + (NBUF > 3 ? BUF_AL : 128) + EXCH + 4 * kUnitPages;
   static constexpr int VRB = (KIND == KIND_SHARED) ? VW : LW;   // row bytes of the V source region
   static constexpr int V_REG = (KIND == KIND_SHARED) ? V_OFF : LAT_OFF;
   static constexpr int FP8_ITEMS = kTile * NSETS * DL / 16;      // 16-code pieces of an fp8 stage
@@ -225,23 +224,30 @@ struct Cfg {
 // Block q covers region bytes [1024q, 1024q + 1024); lane i lands at byte 1024q + 16i.  Blocks
 // are dealt to the NW waves round-robin across all regions of a stage (FIRST is this region's
 // first block in that order), so every wave issues the floor or the ceiling of blocks / NW.
-// `src_row(t)` is the global address of stage token t's row, `src_col(b)` the byte offset in
-// that row of logical LDS row byte b.
-template <int RB, int MSK, int NW, int FIRST, class RowFn, class ColFn>
-__device__ __forceinline__ void dma_region(char* region, int wave, int lane, RowFn src_row, ColFn src_col) {
+// Global source: stage token t's row starts at rows + min(t, tlast) * row_bytes (rows past the
+// unit's end repeat its last row), and logical LDS row byte b comes from byte col(b) of it.  The
+// address is formed as a wave-uniform 64-bit base plus a 32-bit per-lane offset, which the copy
+// instruction takes as an SGPR pair and one VGPR.
+template <int RB, int MSK, int NW, int FIRST, class ColFn>
+__device__ __forceinline__ void dma_region(char* region, int wave, int lane, const char* rows, int row_bytes, int tlast,
+                                           ColFn col) {
   constexpr int blocks = kTile * RB / 1024;
   constexpr int iters = (blocks + NW - 1) / NW;
   constexpr int shift = FIRST % NW;
+  constexpr int CPR = RB / 16;  // 16-byte chunks per row
   const int q0 = wave >= shift ? wave - shift : wave - shift + NW;
 #pragma unroll
   for (int i = 0; i < iters; ++i) {
     const int q = q0 + i * NW;
     if (blocks % NW == 0 || q < blocks) {
-      const int o = q * 1024 + lane * 16;
-      const int t = o >> ilog2(RB);
-      const int cp = (o & (RB - 1)) >> 4;                             // physical chunk in the row
-      const int c = (cp & ~MSK) | ((cp & MSK) ^ (swz_key(t) & MSK));  // logical chunk it must hold
-      dma16(src_row(t) + src_col(c << 4), region + q * 1024);
+      const int t_first = (q * 1024) / RB;                                    // wave-uniform
+      const int t = RB >= 1024 ? t_first : t_first + lane / CPR;              // this lane's row
+      const int cp = RB >= 1024 ? ((q * 1024) % RB) / 16 + lane : lane % CPR;  // physical chunk in it
+      const int c = (cp & ~MSK) | ((cp & MSK) ^ (swz_key(t) & MSK));           // logical chunk it holds
+      const int tu = min(t_first, tlast);
+      unsigned voff = (unsigned)((min(t, tlast) - tu) * row_bytes + col(c << 4));
+      asm volatile("" : "+v"(voff));  // computed here, not hoisted as a 64-bit address per block
+      dma16(rows + (size_t)tu * row_bytes + voff, region + q * 1024);
     }
   }
 }
@@ -266,7 +272,7 @@ __global__ __launch_bounds__(NSETS* HB* SPLIT * 64) void decode_kernel(DecodeArg
   __shared__ __attribute__((aligned(128))) char lds_b2[C::NBUF > 2 ? C::BUF_AL : 128];
   __shared__ __attribute__((aligned(128))) char lds_b3[C::NBUF > 3 ? C::BUF_AL : 128];
   __shared__ __attribute__((aligned(16))) float lds_exch[C::EXCH / 4];
-  __shared__ int lds_pages[kPageCap];
+  __shared__ int lds_pages[kUnitPages];
 
   // XCD-aware mapping: all work groups of one unit land on the same XCD (ids = unit mod 8)
   const int x = blockIdx.x;
@@ -297,11 +303,11 @@ __global__ __launch_bounds__(NSETS* HB* SPLIT * 64) void decode_kernel(DecodeArg
   const int row = a.mlra ? head * G + gs : head;
   const int32_t* __restrict__ bt_row = block_table + (size_t)b * a.max_pages;
   const int page_size = a.page_size;
-  // The unit's first kPageCap block-table entries are staged in LDS up front, so that issuing a
-  // stage's copies waits for an LDS read rather than a dependent scalar load from memory.
+  // The unit's block-table entries (at most kUnitPages) are staged in LDS up front, so that issuing
+  // a stage's copies waits for an LDS read rather than for a dependent scalar load from memory.
   const int first_page = t_begin / page_size;
   const int unit_pages = t_end > t_begin ? (t_end - 1) / page_size - first_page + 1 : 0;
-  for (int i = threadIdx.x; i < unit_pages && i < kPageCap; i += C::THREADS)
+  for (int i = threadIdx.x; i < unit_pages && i < kUnitPages; i += C::THREADS)
     lds_pages[i] = clampi(bt_row[first_page + i], 0, a.num_pages - 1);
   __syncthreads();
 
@@ -316,17 +322,16 @@ __global__ __launch_bounds__(NSETS* HB* SPLIT * 64) void decode_kernel(DecodeArg
   auto issue_stage = [&](int stage0, char* buf) {
     // every token of a stage lies in one page (stages are page aligned and page_size % 32 == 0)
     const int pi = stage0 / page_size - first_page;
-    const int page = pi < kPageCap ? __builtin_amdgcn_readfirstlane(lds_pages[pi])
-                                   : clampi(bt_row[stage0 / page_size], 0, a.num_pages - 1);
+    // a unit spans at most kUnitPages pages (planner rule); the clamp only keeps the read in bounds
+    const int page = __builtin_amdgcn_readfirstlane(lds_pages[min(pi, kUnitPages - 1)]);
     const size_t r0 = (size_t)page * page_size + (stage0 % page_size);
     const int tlast = t_end - 1 - stage0;  // rows past the unit's end repeat its last row
+    const char* krows = kbase + r0 * (size_t)grow_bytes;
     if constexpr (KV != KV_FP8) {
-      dma_region<C::LW, C::MLS, C::DMA_WAVES, 0>(buf + C::LAT_OFF, wave, lane,
-                                [&](int t) { return kbase + (r0 + min(t, tlast)) * (size_t)grow_bytes; },
-                                [&](int cb) {
-                                  const int s2 = cb / (DL * ES);
-                                  return (set0 + s2) * DL * ES + (cb - s2 * DL * ES);
-                                });
+      dma_region<C::LW, C::MLS, C::DMA_WAVES, 0>(buf + C::LAT_OFF, wave, lane, krows, grow_bytes, tlast, [&](int cb) {
+        const int s2 = cb / (DL * ES);
+        return (set0 + s2) * DL * ES + (cb - s2 * DL * ES);
+      });
     } else {
       // codes -> registers now; converted and written after this stage's compute
 #pragma unroll
@@ -345,24 +350,21 @@ __global__ __launch_bounds__(NSETS* HB* SPLIT * 64) void decode_kernel(DecodeArg
     }
     if constexpr (KIND == KIND_LATENT && DR > 0) {
       if constexpr (KV == KV_FP8) {
-        const char* rbase = static_cast<const char*>(a.rope);
-        dma_region<C::RW, C::MR, C::DMA_WAVES, 0>(buf + C::ROPE_OFF, wave, lane,
-                                 [&](int t) { return rbase + (r0 + min(t, tlast)) * (size_t)(DR * 2); },
-                                 [&](int cb) { return cb; });
+        const char* rrows = static_cast<const char*>(a.rope) + r0 * (size_t)(DR * 2);
+        dma_region<C::RW, C::MR, C::DMA_WAVES, 0>(buf + C::ROPE_OFF, wave, lane, rrows, DR * 2, tlast,
+                                                  [&](int cb) { return cb; });
       } else {
-        dma_region<C::RW, C::MR, C::DMA_WAVES, kTile * C::LW / 1024>(buf + C::ROPE_OFF, wave, lane,
-                                 [&](int t) { return kbase + (r0 + min(t, tlast)) * (size_t)grow_bytes; },
-                                 [&](int cb) { return G * DL * ES + cb; });
+        dma_region<C::RW, C::MR, C::DMA_WAVES, kTile * C::LW / 1024>(buf + C::ROPE_OFF, wave, lane, krows, grow_bytes,
+                                                                     tlast, [&](int cb) { return G * DL * ES + cb; });
       }
     }
     if constexpr (KIND == KIND_SHARED) {
-      const char* vbase_g = static_cast<const char*>(a.v);
-      dma_region<C::VW, C::MV, C::DMA_WAVES, kTile *(C::LW + C::RW) / 1024>(buf + C::V_OFF, wave, lane,
-                               [&](int t) { return vbase_g + (r0 + min(t, tlast)) * (size_t)grow_bytes; },
-                               [&](int cb) {
-                                 const int s2 = cb / (DL * ES);
-                                 return (set0 + s2) * DL * ES + (cb - s2 * DL * ES);
-                               });
+      const char* vrows = static_cast<const char*>(a.v) + r0 * (size_t)grow_bytes;
+      dma_region<C::VW, C::MV, C::DMA_WAVES, kTile *(C::LW + C::RW) / 1024>(
+          buf + C::V_OFF, wave, lane, vrows, grow_bytes, tlast, [&](int cb) {
+            const int s2 = cb / (DL * ES);
+            return (set0 + s2) * DL * ES + (cb - s2 * DL * ES);
+          });
     }
   };
   // fp8: convert the prefetched codes and write them (and the scales) into buffer `buf`

@@ -4,6 +4,7 @@
 //   L_b   = clamp(seq_lens[b], 0, capacity)
 //   auto:   chunk = max(page, roundup(ceil(sum_b L_b / target_units), page)); n_b = ceil(L_b / chunk)
 //   forced: chunk_b = max(page, roundup(ceil(L_b / splits), page));        n_b = ceil(L_b / chunk_b)
+//   either chunk is capped at kUnitPages pages
 //   units of sequence b are first_b .. first_b + n_b - 1 (first_b = exclusive prefix sum of n_b),
 //   unit first_b + s covers tokens [s * chunk_b, min(L_b, (s + 1) * chunk_b)).
 //
@@ -48,6 +49,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
       const long long per = (total + a.target_units - 1) / a.target_units;
       long long c = (per + page - 1) / page * page;
       if (c < page) c = page;
+      if (c > (long long)kUnitPages * page) c = (long long)kUnitPages * page;
       chunk = (int)(c > 0x7fffffffLL ? 0x7fffffff : c);
     }
     s_chunk = chunk;
@@ -67,6 +69,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
         const int per = (L + a.forced_splits - 1) / a.forced_splits;
         ck = (per + page - 1) / page * page;
         if (ck < page) ck = page;
+        if (ck > kUnitPages * page) ck = kUnitPages * page;
       }
       n = (L + ck - 1) / ck;
     }
