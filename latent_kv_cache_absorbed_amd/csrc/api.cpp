@@ -191,15 +191,23 @@ int32_t ld_plan_host(const ld_problem* p, const int32_t* seq_lens_host, int32_t 
   const long long cap = (long long)p->max_pages_per_seq * p->page_size;
   const int page = p->page_size;
   auto clampL = [&](int32_t L) -> long long { return L < 0 ? 0 : (L > cap ? cap : L); };
-  long long total = 0;
-  for (int b = 0; b < p->batch; ++b) total += clampL(seq_lens_host[b]);
   long long chunk = 0;
   if (p->num_splits == 0) {
+    // the smallest multiple of the page that gives at most `target` units (bisection on pages)
     const long long target = target_units_for(*p, num_cus);
-    const long long per = (total + target - 1) / target;
-    chunk = (per + page - 1) / page * page;
-    if (chunk < page) chunk = page;
-    if (chunk > (long long)kUnitPages * page) chunk = (long long)kUnitPages * page;
+    long long mx = 0;
+    for (int b = 0; b < p->batch; ++b) mx = std::max(mx, clampL(seq_lens_host[b]));
+    long long lo = 1, hi = std::max(1LL, (mx + page - 1) / page);
+    while (lo < hi) {
+      const long long mid = (lo + hi) / 2, c = mid * page;
+      long long cnt = 0;
+      for (int b = 0; b < p->batch; ++b) cnt += (clampL(seq_lens_host[b]) + c - 1) / c;
+      if (cnt <= target)
+        hi = mid;
+      else
+        lo = mid + 1;
+    }
+    chunk = std::min(lo, (long long)kUnitPages) * page;
   }
   long long units = 0;
   for (int b = 0; b < p->batch; ++b) {

@@ -18,7 +18,7 @@ enum Kind : int {
 
 constexpr int kTile = 32;            // tokens per MFMA tile (one 32-row block)
 constexpr int kWaveSize = 64;
-constexpr int kPlanThreads = 1024;
+constexpr int kPlanThreads = 256;
 constexpr int kCombineChunk = 16;     // splits merged by one combine task
 constexpr int kUnitPages = 512;       // pages a work unit spans at most (its block-table entries fit in LDS)
 

@@ -142,6 +142,16 @@ def test_planner_balances_one_long_sequence():
     assert units == 256 and chunk == 4096
 
 
+def test_planner_fills_the_chip_in_one_round_for_ragged_lengths():
+    # ragged lengths: the chunk is the smallest page multiple giving at most one unit per CU
+    lens = np.random.default_rng(7).integers(1024, 65537, size=64).astype(np.int32)
+    p = mla(batch=64, max_pages_per_seq=1024, num_pages=64 * 1024 + 1)
+    chunk, units, ns, _ = lkd.plan_host(p, lens, 256)
+    assert units <= 256 and chunk % 64 == 0
+    smaller = chunk - 64
+    assert smaller < 64 or int(np.sum(-(-lens.astype(np.int64) // smaller))) > 256
+
+
 def test_planner_splits_batch_decode_across_the_chip():
     p = mla(batch=64, max_pages_per_seq=64, num_pages=4097)
     chunk, units, ns, _ = lkd.plan_host(p, np.full(64, 4096, np.int32), 256)
