@@ -317,9 +317,8 @@ __global__ __launch_bounds__(NSETS* HB* SPLIT * 64) void decode_kernel(DecodeArg
   const char* kbase = static_cast<const char*>(a.k);
 
   // ---- issue the copies of one stage into buffer `buf`
-  // fp8: the codes (and scales) of two stages in flight, in alternating register sets
-  uint4 pre[2][C::FP8_PER_THREAD];
-  float pre_sc[2] = {0.f, 0.f};
+  uint4 pre[C::FP8_PER_THREAD];
+  float pre_sc = 0.f;
   auto issue_stage = [&](int stage0, char* buf) {
     // every token of a stage lies in one page (stages are page aligned and page_size % 32 == 0)
     const int pi = stage0 / page_size - first_page;
@@ -333,6 +332,21 @@ __global__ __launch_bounds__(NSETS* HB* SPLIT * 64) void decode_kernel(DecodeArg
         const int s2 = cb / (DL * ES);
         return (set0 + s2) * DL * ES + (cb - s2 * DL * ES);
       });
+    } else {
+      // codes -> registers now; converted and written after this stage's compute
+#pragma unroll
+      for (int r = 0; r < C::FP8_PER_THREAD; ++r) {
+        const int i = threadIdx.x + r * C::THREADS;
+        if (i < C::FP8_ITEMS) {
+          const int t = i / (NSETS * DL / 16);
+          const int k16 = i - t * (NSETS * DL / 16);
+          const int s2 = (k16 * 16) / DL;
+          const int w = k16 * 16 - s2 * DL;
+          pre[r] = *reinterpret_cast<const uint4*>(kbase + (r0 + min(t, tlast)) * (size_t)grow_bytes +
+                                                   (size_t)(set0 + s2) * DL + w);
+        }
+      }
+      if (threadIdx.x < kTile) pre_sc = a.kscale[r0 + min((int)threadIdx.x, tlast)];
     }
     if constexpr (KIND == KIND_LATENT && DR > 0) {
       if constexpr (KV == KV_FP8) {
@@ -353,32 +367,8 @@ __global__ __launch_bounds__(NSETS* HB* SPLIT * 64) void decode_kernel(DecodeArg
           });
     }
   };
-  // fp8: load a stage's codes (16 per thread and item) and scales into register set `set`.  Every
-  // thread issues exactly FP8_PER_THREAD code loads (items past the end repeat the last one), so
-  // the count of loads in flight is known when waiting for the copies issued before them.
-  auto issue_codes = [&](int stage0, int set) __attribute__((always_inline)) {
-    if constexpr (KV == KV_FP8) {
-      const int pi = stage0 / page_size - first_page;
-      const int page = __builtin_amdgcn_readfirstlane(lds_pages[min(pi, kUnitPages - 1)]);
-      const size_t r0 = (size_t)page * page_size + (stage0 % page_size);
-      const int tlast = t_end - 1 - stage0;
-#pragma unroll
-      for (int r = 0; r < C::FP8_PER_THREAD; ++r) {
-        const int i = min((int)threadIdx.x + r * C::THREADS, C::FP8_ITEMS - 1);
-        const int t = i / (NSETS * DL / 16);
-        const int k16 = i - t * (NSETS * DL / 16);
-        const int s2 = (k16 * 16) / DL;
-        const int w = k16 * 16 - s2 * DL;
-        pre[set][r] = *reinterpret_cast<const uint4*>(kbase + (r0 + min(t, tlast)) * (size_t)grow_bytes +
-                                                      (size_t)(set0 + s2) * DL + w);
-      }
-      if (threadIdx.x < kTile) pre_sc[set] = a.kscale[r0 + min((int)threadIdx.x, tlast)];
-    }
-    (void)stage0;
-    (void)set;
-  };
-  // fp8: convert register set `set` and write the codes (and the scales) into buffer `buf`
-  auto finish_stage = [&](char* buf, int set) {
+  // fp8: convert the prefetched codes and write them (and the scales) into buffer `buf`
+  auto finish_stage = [&](char* buf) {
     if constexpr (KV == KV_FP8) {
 #pragma unroll
       for (int r = 0; r < C::FP8_PER_THREAD; ++r) {
@@ -387,16 +377,14 @@ __global__ __launch_bounds__(NSETS* HB* SPLIT * 64) void decode_kernel(DecodeArg
           const int t = i / (NSETS * DL / 16);
           const int k16 = i - t * (NSETS * DL / 16);
           char* rowp = buf + C::LAT_OFF;
-          *reinterpret_cast<uint4*>(rowp + lds_off(t, C::LW, C::MLS, k16 * 32)) =
-              e4m3x8_to_bf16x8(pre[set][r].x, pre[set][r].y);
+          *reinterpret_cast<uint4*>(rowp + lds_off(t, C::LW, C::MLS, k16 * 32)) = e4m3x8_to_bf16x8(pre[r].x, pre[r].y);
           *reinterpret_cast<uint4*>(rowp + lds_off(t, C::LW, C::MLS, k16 * 32 + 16)) =
-              e4m3x8_to_bf16x8(pre[set][r].z, pre[set][r].w);
+              e4m3x8_to_bf16x8(pre[r].z, pre[r].w);
         }
       }
-      if (threadIdx.x < kTile) reinterpret_cast<float*>(buf + C::SC_OFF)[threadIdx.x] = pre_sc[set];
+      if (threadIdx.x < kTile) reinterpret_cast<float*>(buf + C::SC_OFF)[threadIdx.x] = pre_sc;
     }
     (void)buf;
-    (void)set;
   };
 
   // ---- this lane's query fragments (B operand of S^T = K . Q^T) for the wave's k-steps:
@@ -480,13 +468,7 @@ __global__ __launch_bounds__(NSETS* HB* SPLIT * 64) void decode_kernel(DecodeArg
     for (int n = 0; n < NB - 1; ++n)
       if (n < nstage) issue_stage(t_begin + n * kTile, bufs[n]);
   }
-  if constexpr (KV == KV_FP8) {
-    // stage 0's codes converted now, stage 1's in flight; stage n+2's are loaded during stage n
-    if (nstage > 0) issue_codes(t_begin, 0);
-    __builtin_amdgcn_s_waitcnt(0);
-    finish_stage(bufs[0], 0);
-    if (nstage > 1) issue_codes(t_begin + kTile, 1);
-  }
+  finish_stage(bufs[0]);
 
   // The work on a stage has two parts.  part_s: this wave's (partial) scores, into sp; with
   // SPLIT = 2 they are posted for the partner wave.  part_pv: (the partner's half added) the online
@@ -673,11 +655,7 @@ __global__ __launch_bounds__(NSETS* HB* SPLIT * 64) void decode_kernel(DecodeArg
     // this wave's copies of stage n have landed; those of the (up to NB-2) later stages already
     // issued may stay in flight
     if constexpr (KV == KV_FP8) {
-      // the RoPE copies of stage n, issued before the codes of stage n+1 (which may stay in flight)
-      if (n + 1 < nstage)
-        wait_vmcnt<C::FP8_PER_THREAD>();
-      else
-        wait_vmcnt<0>();
+      __builtin_amdgcn_s_waitcnt(0);
     } else {
       const int later = min(nstage - 1 - n, NB - 2);
       if (later >= 2 && NB >= 4)
@@ -692,16 +670,11 @@ __global__ __launch_bounds__(NSETS* HB* SPLIT * 64) void decode_kernel(DecodeArg
     if (!late) wait_stage(n);
     lds_barrier();
     if (!PP && n + NB - 1 < nstage) issue_stage(t_begin + (n + NB - 1) * kTile, refill);
-    if constexpr (KV == KV_FP8) {
-      __builtin_amdgcn_sched_barrier(0);  // the codes' loads are issued after the RoPE copies
-      if (n + 2 < nstage) issue_codes(t_begin + (n + 2) * kTile, n & 1);
-      __builtin_amdgcn_sched_barrier(0);
-    }
     part_s(cur);
     if constexpr (PP || SPLIT == 2) lds_barrier();
     if (PP && !late && n + NB - 1 < nstage) issue_stage(t_begin + (n + NB - 1) * kTile, refill);
     part_pv(n, cur);
-    if (n + 1 < nstage) finish_stage(nxt, (n + 1) & 1);
+    if (n + 1 < nstage) finish_stage(nxt);
   };
 
   if (late) lds_barrier();
