@@ -13,6 +13,8 @@
 // log-sum-exps lse_s:  lse = ln sum_s exp(lse_s),  o = sum_s exp(lse_s - lse) o_s.
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "ld_internal.h"
 
 namespace ld {
@@ -258,10 +260,11 @@ constexpr int kBatch = 8;
 
 struct Merge {
   float M = -INFINITY, tot = 0.f, o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  template <int KB = kBatch>
   __device__ __forceinline__ void add(const float* ls, const float (*v)[8], int valid, int vals) {
     float bm = -INFINITY;
 #pragma unroll
-    for (int k = 0; k < kBatch; ++k)
+    for (int k = 0; k < KB; ++k)
       if (k < valid) bm = fmaxf(bm, ls[k]);
     const float Mn = fmaxf(M, bm);
     if (Mn == -INFINITY) return;
@@ -270,7 +273,7 @@ struct Merge {
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[e] *= r;
 #pragma unroll
-    for (int k = 0; k < kBatch; ++k) {
+    for (int k = 0; k < KB; ++k) {
       const float w = k < valid ? expf(ls[k] - Mn) : 0.f;
       tot += w;
 #pragma unroll
@@ -289,7 +292,51 @@ struct Merge {
   }
 };
 
+// The 4 waves of a work group hold 32 heads x 32 (f32) or 64 (bf16) consecutive columns of the
+// output; a sequence finished here passes them through LDS so that every store writes 16 bytes of
+// a row and each row segment is written whole (128 B per head).
+__device__ __forceinline__ void write_tile(const DecodeArgs& a, int d_v, const PieceGroup& p, int b, const float* o,
+                                          float lse, float* tile) {
+  const int vals = a.part_bf16 ? 8 : 4;
+  const int tcols = 8 * vals;  // 4 pieces of 16 / vals per 32-column block: 32 (f32) or 64 (bf16) columns
+  const int row_l = p.lane & 31;
+  // value e of piece j is register i = vals * j + e: column 32 cb + 8 (i / 4) + 4 h + i % 4
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    if (e < vals) {
+      const int i = vals * p.j + e;
+      const int colg = 32 * p.cb + 8 * (i / 4) + 4 * p.h + (i % 4);
+      tile[row_l * (tcols + 1) + (colg % tcols)] = o[e];
+    }
+  }
+  if (p.cb == 0 && p.j == 0 && p.h == 0 && p.head_in_set < a.heads_per_set) {
+    const int row = a.mlra ? p.head_in_set * a.groups + p.gs : p.gs * a.heads_per_set + p.head_in_set;
+    a.lse[(size_t)b * a.rows + row] = lse;
+  }
+  __syncthreads();
+  // thread -> (row, 16-byte chunk): 32 rows x 8 chunks (bf16: 8 values, f32: 4 values)
+  const int r = threadIdx.x >> 3, ch = threadIdx.x & 7;
+  const int head_in_set = p.hb * 32 + r;
+  const int col0 = (32 * p.cb) / tcols * tcols;  // first column of the tile
+  if (head_in_set < a.heads_per_set) {
+    const int row = a.mlra ? head_in_set * a.groups + p.gs : p.gs * a.heads_per_set + head_in_set;
+    const size_t orow = (size_t)b * a.rows + row;
+    const float* src = tile + r * (tcols + 1) + ch * (vals == 8 ? 8 : 4);
+    if (a.out_bf16) {
+      typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+      bf16x8_t v;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = (__bf16)src[e];
+      *reinterpret_cast<bf16x8_t*>(static_cast<__bf16*>(a.out) + orow * d_v + col0 + ch * 8) = v;
+    } else {
+      *reinterpret_cast<float4*>(static_cast<float*>(a.out) + orow * d_v + col0 + ch * 4) =
+          make_float4(src[0], src[1], src[2], src[3]);
+    }
+  }
+}
+
 __global__ __launch_bounds__(kCombineThreads) void combine_ws_kernel(DecodeArgs a, int d_v) {
+  __shared__ float tile[32 * 65];
   const int t = blockIdx.y;
   if (t >= a.header[2]) return;
   const int b = a.tasks[2 * t];
@@ -304,10 +351,12 @@ __global__ __launch_bounds__(kCombineThreads) void combine_ws_kernel(DecodeArgs 
   const int s_lo = c * kCombineChunk;
   const int cnt = max(0, min(n - s_lo, kCombineChunk));  // splits of this chunk
   Merge m;
-  for (int k0 = 0; k0 < cnt; k0 += kBatch) {
-    float ls[kBatch], v[kBatch][8];
+  // one batch of KB (lse, piece) pairs, loads issued together; indexes past the last repeat it
+  auto batch = [&](auto kb, int k0) {
+    constexpr int KB = decltype(kb)::value;
+    float ls[KB], v[KB][8];
 #pragma unroll
-    for (int k = 0; k < kBatch; ++k) {
+    for (int k = 0; k < KB; ++k) {
       const size_t s = first + s_lo + min(k0 + k, cnt - 1);
       ls[k] = a.part_lse[(s * p.blocks_per_unit + p.blk_in_unit) * 32 + (p.lane & 31)];
       const size_t off = (s * p.blocks_per_unit + p.blk_in_unit) * (size_t)(32 * d_v) + p.piece_off;
@@ -322,11 +371,16 @@ __global__ __launch_bounds__(kCombineThreads) void combine_ws_kernel(DecodeArgs 
         v[k][4] = v[k][5] = v[k][6] = v[k][7] = 0.f;
       }
     }
-    m.add(ls, v, cnt - k0, vals);
+    m.add<KB>(ls, v, cnt - k0, vals);
+  };
+  if (cnt <= 4) {
+    if (cnt > 0) batch(std::integral_constant<int, 4>{}, 0);
+  } else {
+    for (int k0 = 0; k0 < cnt; k0 += kBatch) batch(std::integral_constant<int, kBatch>{}, k0);
   }
   if (nc <= 1) {
     const float lse = m.finish();
-    write_piece(a, d_v, p, b, m.o, lse);
+    write_tile(a, d_v, p, b, m.o, lse, tile);
     return;
   }
   // a chunk of a longer sequence: its merged result, for combine_chunks_kernel
