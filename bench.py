@@ -176,6 +176,9 @@ def main() -> int:
     ap.add_argument("--workload", default="mla_b64_l4k")
     ap.add_argument("--copies", type=int, default=4, help="cache copies rotated across steps")
     ap.add_argument("--num-splits", type=int, default=0)
+    ap.add_argument("--graph", action="store_true",
+                    help="time each step as the replay of a HIP graph holding its plan, decode and combine launches "
+                         "(the eager time is reported too); default: eager launches")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -232,16 +235,42 @@ def main() -> int:
         decs[i % len(decs)].run()
     torch.cuda.synchronize()
 
-    # ---- the timed steps: plan + decode + combine, K times back to back
+    # ---- the timed steps: plan + decode + combine, K times back to back, launched eagerly; with
+    # --graph each step is instead the replay of a HIP graph holding the step's launches (one graph per
+    # cache copy), and the eager time is reported beside it
     K = args.steps
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record(stream)
-    for i in range(K):
-        decs[i % len(decs)].run()
-    stop.record(stream)
-    torch.cuda.synchronize()
-    total_ms = start.elapsed_time(stop)
+
+    def time_steps(step):
+        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record(stream)
+        for i in range(K):
+            step(i)
+        stop.record(stream)
+        torch.cuda.synchronize()
+        return start.elapsed_time(stop)
+
+    eager_ms = time_steps(lambda i: decs[i % len(decs)].run())
+    graphs = []
+    if args.graph:
+        cap = torch.cuda.Stream(dev)
+        cap.wait_stream(stream)
+        with torch.cuda.stream(cap):
+            for d in decs:
+                d.run()                       # one eager run on the capture stream first
+        torch.cuda.synchronize()
+        for d in decs:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=cap):
+                d.run()
+            graphs.append(g)
+        torch.cuda.synchronize()
+        for g in graphs:
+            g.replay()
+        torch.cuda.synchronize()
+        total_ms = time_steps(lambda i: graphs[i % len(graphs)].replay())
+    else:
+        total_ms = eager_ms
 
     # ---- per-stage kernel durations: each stage launched K times back to back (the plan only depends
     # on seq_lens, so one plan serves every decode and combine launch), per-launch average
@@ -320,6 +349,8 @@ def main() -> int:
                      "traffic": traffic, "alg_bytes_per_launch": int(dec_alg_bytes),
                      "mfma_tflops": round(mfma_tflops, 2), "mfma_frac": round(mfma_tflops / mfma_peak, 4),
                      "flops_per_launch": int(flops), "decode_source_sha": source_sha()},
+        "launch": "hip_graph" if args.graph else "eager",
+        "eager_ms_per_step": round(eager_ms / K, 5),
         "input_gen_s": round(gen_s, 2),
     }
     if not args.no_cpu_baseline:

@@ -85,6 +85,15 @@ WORKLOADS = {
     # GLA-2 over an fp8 latent cache with imbalanced lengths
     "gla2_fp8_b64_mixed": Workload("gla2_fp8_b64_mixed", "gla", 64, 128, 2, 256, 64, ("uniform", 1024, 65536),
                                    kv_dtype="fp8_e4m3", scale=_S192, seed=5),
+    # one GPU's share under the tensor-parallel layouts the pages describe: one MLRA-4 branch (all
+    # 128 heads, a 128-dim latent block + the shared rope key) under TP-4, and one GLA-2 latent group
+    # (its 64 heads, a 256-dim latent + rope) under TP-2
+    "mlra4_tp4_share_b1_l128k": Workload("mlra4_tp4_share_b1_l128k", "mlra", 1, 128, 1, 128, 64, 131072,
+                                         scale=_S192, seed=3),
+    "mlra4_tp4_share_b1_l1m": Workload("mlra4_tp4_share_b1_l1m", "mlra", 1, 128, 1, 128, 64, 1048576,
+                                       scale=_S192, seed=3),
+    "gla2_tp2_share_fp8_b64_mixed": Workload("gla2_tp2_share_fp8_b64_mixed", "gla", 64, 64, 1, 256, 64,
+                                             ("uniform", 1024, 65536), kv_dtype="fp8_e4m3", scale=_S192, seed=5),
 }
 
 

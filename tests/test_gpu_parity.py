@@ -71,6 +71,20 @@ def test_gla2(kv):
     _check(inp)
 
 
+# --- one GPU's tensor-parallel share: one MLRA-4 branch (128 heads, 128 + 64 dims) and one GLA-2
+# group (64 heads, 256 + 64 dims)
+def test_mlra4_one_branch():
+    inp = synth.make_inputs("mlra", 2, 128, 1, 128, 64, [900, 65], scale=1 / math.sqrt(192), seed=21)
+    _check(inp)
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8_e4m3"])
+def test_gla2_one_group(kv):
+    inp = synth.make_inputs("gla", 3, 64, 1, 256, 64, [1, 700, 1300], scale=1 / math.sqrt(192), seed=22,
+                            kv_dtype=kv)
+    _check(inp)
+
+
 def test_mla_fp8():
     inp = synth.make_inputs("mla", 2, 128, 1, 512, 64, [600, 65], scale=1 / math.sqrt(192), seed=15,
                             kv_dtype="fp8_e4m3")
@@ -150,3 +164,36 @@ def test_mla_bf16_one_long_sequence_many_splits():
 def test_mla_bf16_forced_many_splits(splits):
     inp = synth.make_inputs("mla", 3, 128, 1, 512, 64, [5000, 64, 2600], scale=1 / math.sqrt(192), seed=23)
     _check(inp, num_splits=splits)
+
+
+# --- the whole step (plan + decode + one- and two-level combine) captured in a HIP graph: every
+# replay, with eager work on the same buffers in between, reproduces the eager result bit for bit
+@pytest.mark.parametrize("lens", [[1500, 77, 3000], [40000]])
+def test_graph_replay_matches_eager(lens):
+    import latent_kv_cache_absorbed_amd as lkd
+    from gpu_util import to_dev
+    inp = synth.make_inputs("mla", len(lens), 128, 1, 512, 64, lens, scale=1 / math.sqrt(192), seed=23)
+    print(f"case graph replay lens={lens}", flush=True)
+    bt = torch.from_numpy(inp.layout.block_table).cuda()
+    sl = torch.from_numpy(inp.layout.seq_lens).cuda()
+    d = lkd.Decoder(to_dev(inp.q_lat), to_dev(inp.q_rope), to_dev(inp.k_pool), bt, sl, variant="mla",
+                    scale=inp.scale)
+    out0, lse0 = (t.clone() for t in d.run())
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        d.run()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        d.run()
+    torch.cuda.synchronize()
+    for r in range(4):
+        d.out.fill_(float("nan"))
+        d.lse.fill_(float("nan"))
+        d.workspace.fill_(0xFF)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(d.out, out0) and torch.equal(d.lse, lse0), f"replay {r} differs from the eager run"
