@@ -12,3 +12,4 @@ open; its invariants are pinned, its pair layout and base are a reading
 (parity unpinned for the flavour, and the GPU path never applies RoPE).
 """
 from .attention import *  # noqa: F401,F403
+from .cache import *  # noqa: F401,F403
