@@ -181,6 +181,28 @@ int32_t ld_split_kv_combine(int32_t num_rows, int32_t d_v, int32_t max_splits, c
                             const float* partial_lse, const int32_t* row_num_splits, int32_t out_dtype, void* out,
                             float* lse, void* stream);
 
+/* Append the decode step's new token of every sequence to the paged latent cache (latent variants:
+ * MLA, GLA, MLRA).  This is the step that precedes the attention: the cached row of a token is its
+ * latent c^KV followed by its decoupled RoPE key k^R, already rotated (MLA explainer, mlqm.cn news
+ * 371735, sections 2.2 and 2.4; MLRA article, MLA paragraph: only the latent and the RoPE key are
+ * cached); the fp8 cache follows the FP8 serving of the GTA/GLA article (jsbsmhs.com).
+ *   For sequence b with L = seq_lens[b] >= 1 (the length counting the new token) the token goes to
+ *   logical position pos = L - 1: physical page block_table[b*max_pages_per_seq + pos / page_size],
+ *   slot pos % page_size.  Sequences with L <= 0 are left alone.
+ *   c_new   [B, G*d_latent]: the token's latent row (all groups), in q_dtype (F32 or BF16)
+ *   kr_new  [B, d_rope]: its RoPE key before rotation, in q_dtype; d_rope must be even
+ *   RoPE:   pair (2i, 2i+1) turns by pos * rope_base^(-2i/d_rope) (angle, cosine, sine and rotation
+ *           in fp64, then rounded to the cache dtype); rope_base > 0 and finite
+ *   kv_dtype F32/BF16: cache->k row = [latent | rotated key], converted with round to nearest even
+ *   kv_dtype FP8_E4M3: one scale per token, scale = amax|latent| / 448 in fp32 (1 for a zero row);
+ *           cache->k gets the E4M3 code nearest to latent / scale (fp32 division, clamped to +-448,
+ *           ties to the even code), cache->scale the scale, cache->rope the rotated key in bf16.
+ * The problem's num_q_heads, out_dtype, softmax_scale and num_splits are not used.  The cache
+ * pointers are written through (the memory must be writable).  GQA/MQA/GTA give LD_ERR_UNSUPPORTED.
+ * Asynchronous on `stream`; a failed call queues nothing. */
+int32_t ld_cache_append(const ld_problem* p, const void* c_new, const void* kr_new, const int32_t* block_table,
+                        const int32_t* seq_lens, const ld_kv_cache* cache, float rope_base, void* stream);
+
 /* Host check of the metadata: 0 <= seq_lens[b] <= max_pages_per_seq*page_size
  * and every block_table entry a sequence uses lies in [0, num_pages).
  * LD_OK or LD_ERR_BAD_METADATA (or a pointer/shape error). */

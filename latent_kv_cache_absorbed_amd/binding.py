@@ -18,6 +18,7 @@ import torch
 __all__ = [
     "LatentDecodeError", "Decoder", "lib", "library_path", "Problem", "KVCache", "VARIANTS", "DTYPES",
     "make_problem", "workspace_size", "latent_decode", "split_kv_combine", "validate_metadata", "plan_host",
+    "cache_append",
     "check_problem", "status_string", "header_functions",
 ]
 
@@ -79,6 +80,8 @@ def lib():
         L.ld_decode_planned.argtypes = [P, vp, vp, ctypes.POINTER(KVCache), vp, vp, vp, vp, vp, sz, vp]
         L.ld_combine_planned.restype = i32
         L.ld_combine_planned.argtypes = [P, vp, vp, vp, sz, vp]
+        L.ld_cache_append.restype = i32
+        L.ld_cache_append.argtypes = [P, vp, vp, vp, vp, ctypes.POINTER(KVCache), ctypes.c_float, vp]
         L.ld_split_kv_combine.restype = i32
         L.ld_split_kv_combine.argtypes = [i32, i32, i32, vp, vp, vp, i32, vp, vp, vp]
         L.ld_validate_metadata.restype = i32
@@ -251,6 +254,41 @@ def latent_decode(q_latent, q_rope, k, block_table, seq_lens, *, variant: str, s
                 rope=rope, kscale=kscale, out=out, lse=lse, out_dtype=out_dtype, num_splits=num_splits,
                 workspace=workspace)
     return d.run(stream)
+
+
+def cache_append(c_new, kr_new, k, block_table, seq_lens, *, variant: str = "mla", groups: int = 1,
+                 rope_base: float = 10000.0, rope=None, kscale=None, stream=None):
+    """ld_cache_append: write each sequence's new token (at position seq_lens[b] - 1) into the paged cache.
+
+    c_new [B, groups * d_latent] and kr_new [B, d_rope] (un-rotated) in f32 or bf16; ``k`` is the
+    cache (f32/bf16 rows [P, page, G*d_latent + d_rope], or fp8 codes [P, page, G*d_latent] with the
+    bf16 ``rope`` pool and the f32 ``kscale`` pool beside it), updated in place.
+    """
+    if variant not in ("mla", "gla", "mlra"):
+        raise ValueError("cache_append covers the latent variants (mla, gla, mlra)")
+    _need(c_new, "c_new", (torch.float32, torch.bfloat16))
+    _need(kr_new, "kr_new", (c_new.dtype,))
+    _need(k, "k", tuple(_TORCH_DTYPE))
+    _need(block_table, "block_table", (torch.int32,))
+    _need(seq_lens, "seq_lens", (torch.int32,))
+    kv_dtype = _TORCH_DTYPE[k.dtype]
+    if kv_dtype == "fp8_e4m3":
+        _need(rope, "rope", (torch.bfloat16,))
+        _need(kscale, "kscale", (torch.float32,))
+    B, D = c_new.shape
+    dr = kr_new.shape[-1]
+    if D % groups:
+        raise ValueError("c_new's width is not groups * d_latent")
+    p = make_problem(variant, B, groups, groups, D // groups, dr, k.shape[1], k.shape[0], block_table.shape[1],
+                     _TORCH_DTYPE[c_new.dtype], kv_dtype, "f32", 1.0)
+    cache = KVCache(k.data_ptr(), None if rope is None else rope.data_ptr(), None,
+                    None if kscale is None else kscale.data_ptr())
+    if stream is None:
+        stream = torch.cuda.current_stream(c_new.device).cuda_stream
+    st = lib().ld_cache_append(ctypes.byref(p), _ptr(c_new), _ptr(kr_new), _ptr(block_table), _ptr(seq_lens),
+                               ctypes.byref(cache), float(rope_base), ctypes.c_void_p(stream))
+    if st:
+        raise LatentDecodeError(st, "ld_cache_append")
 
 
 def split_kv_combine(partial_out, partial_lse, row_num_splits, *, out_dtype: str = "f32", out=None, lse=None,

@@ -404,6 +404,48 @@ int32_t ld_latent_decode(const ld_problem* p, const void* q_latent, const void* 
   return ld_combine_planned(p, out, lse, workspace, workspace_bytes, stream);
 }
 
+int32_t ld_cache_append(const ld_problem* p, const void* c_new, const void* kr_new, const int32_t* block_table,
+                        const int32_t* seq_lens, const ld_kv_cache* cache, float rope_base, void* stream) {
+  if (!p || !cache) return LD_ERR_NULL_POINTER;
+  if (p->struct_size != sizeof(ld_problem)) return LD_ERR_BAD_STRUCT;
+  if (!latent(*p)) return LD_ERR_UNSUPPORTED;
+  if (p->batch < 0 || p->num_groups < 1 || p->d_latent < 1 || p->d_rope < 0 || (p->d_rope & 1))
+    return LD_ERR_BAD_SHAPE;
+  if (p->variant == LD_VARIANT_MLA && p->num_groups != 1) return LD_ERR_BAD_SHAPE;
+  if (p->page_size < 1 || p->page_size > (1 << 20) || p->num_pages < 1 || p->max_pages_per_seq < 1)
+    return LD_ERR_BAD_SHAPE;
+  if ((long long)p->max_pages_per_seq * p->page_size > 0x7fffffffLL) return LD_ERR_BAD_SHAPE;
+  if ((long long)p->num_groups * p->d_latent > (1 << 24)) return LD_ERR_BAD_SHAPE;
+  if (!std::isfinite(rope_base) || !(rope_base > 0.f)) return LD_ERR_BAD_SHAPE;
+  if (p->q_dtype != LD_F32 && p->q_dtype != LD_BF16) return LD_ERR_BAD_DTYPE;
+  if (p->kv_dtype != LD_F32 && p->kv_dtype != LD_BF16 && p->kv_dtype != LD_FP8_E4M3) return LD_ERR_BAD_DTYPE;
+  if (p->batch == 0) return LD_OK;
+  const bool fp8 = p->kv_dtype == LD_FP8_E4M3;
+  if (!c_new || (p->d_rope > 0 && !kr_new) || !block_table || !seq_lens || !cache->k) return LD_ERR_NULL_POINTER;
+  if (fp8 && (!cache->scale || (p->d_rope > 0 && !cache->rope))) return LD_ERR_NULL_POINTER;
+  if (!aligned(c_new, 16) || (kr_new && !aligned(kr_new, 16)) || !aligned(cache->k, 16) || !aligned(block_table, 4) ||
+      !aligned(seq_lens, 4))
+    return LD_ERR_MISALIGNED;
+  if (fp8 && (!aligned(cache->scale, 4) || (cache->rope && !aligned(cache->rope, 16)))) return LD_ERR_MISALIGNED;
+  AppendArgs a{};
+  a.c_new = c_new;
+  a.kr_new = kr_new;
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  a.k = const_cast<void*>(cache->k);
+  a.rope = const_cast<void*>(cache->rope);
+  a.scale = const_cast<float*>(cache->scale);
+  a.batch = p->batch;
+  a.d_lat = p->num_groups * p->d_latent;
+  a.d_rope = p->d_rope;
+  a.page_size = p->page_size;
+  a.num_pages = p->num_pages;
+  a.max_pages = p->max_pages_per_seq;
+  a.in_bf16 = p->q_dtype == LD_BF16;
+  a.rope_base = rope_base;
+  return launch_append(a, p->kv_dtype, stream) == 0 ? LD_OK : LD_ERR_HIP;
+}
+
 int32_t ld_split_kv_combine(int32_t num_rows, int32_t d_v, int32_t max_splits, const float* partial_out,
                             const float* partial_lse, const int32_t* row_num_splits, int32_t out_dtype, void* out,
                             float* lse, void* stream) {

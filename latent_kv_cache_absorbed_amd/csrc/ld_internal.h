@@ -116,6 +116,21 @@ int launch_combine_rows(int32_t num_rows, int32_t d_v, int32_t max_splits, const
                         void* stream);
 // Returns hipError_t, or -1 when no kernel is built for the shape.
 int launch_decode(const ld_problem& p, const DecodeArgs& a, void* stream);
+
+// one decode step's token appended to the paged latent cache (append.hip)
+struct AppendArgs {
+  const void* c_new;            // [B, d_lat] latent rows (all groups), bf16 or f32
+  const void* kr_new;           // [B, d_rope] un-rotated RoPE keys, same dtype
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  void* k;                      // cache rows (f32/bf16: [.., d_lat + d_rope]; fp8: codes [.., d_lat])
+  void* rope;                   // fp8 cache: bf16 rope pool
+  float* scale;                 // fp8 cache: per-token scale
+  int32_t batch, d_lat, d_rope, page_size, num_pages, max_pages;
+  int32_t in_bf16;
+  float rope_base;
+};
+int launch_append(const AppendArgs& a, int kv_dtype, void* stream);
 // Whether a decode kernel is built for p's dtype/dims/kind with `nsets` sets per work group and
 // `hblocks` 32-head blocks per set.
 bool decode_instantiated(const ld_problem& p, int nsets, int hblocks);

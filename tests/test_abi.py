@@ -102,6 +102,27 @@ def test_combine_rejects_bad_arguments():
     assert L.ld_split_kv_combine(0, 8, 2, None, None, None, 0, None, None, None) == OK
 
 
+def test_append_rejects_before_touching_memory():
+    L = lkd.lib()
+    g = ctypes.c_void_p(0x10000)
+    cache = lkd.KVCache(0x20000, None, None, None)
+    call = lambda p, c=g, kr=g, bt=g, sl=g, cch=cache, base=10000.0: L.ld_cache_append(  # noqa: E731
+        ctypes.byref(p), c, kr, bt, sl, ctypes.byref(cch), base, None)
+    assert call(mla(), c=None) == NULLP
+    assert call(mla(), kr=None) == NULLP
+    assert call(mla(), c=ctypes.c_void_p(0x10008)) == MISAL
+    assert call(mla(), base=0.0) == SHAPE
+    assert call(mla(), base=float("nan")) == SHAPE
+    assert call(mla(d_rope=63)) == SHAPE
+    assert call(mla(q_dtype="fp8_e4m3")) == DTYPE
+    assert call(mla(variant="gqa", heads=64, groups=8, d_latent=128, d_rope=0)) == UNSUP
+    assert call(mla(kv_dtype="fp8_e4m3")) == NULLP                 # rope / scale pools missing
+    p = mla()
+    p.struct_size = 4
+    assert call(p) == STRUCT
+    assert call(mla(batch=0), c=None, kr=None, bt=None, sl=None) == OK
+
+
 def test_workspace_grows_with_forced_splits():
     assert lkd.workspace_size(mla(num_splits=16)) > lkd.workspace_size(mla(num_splits=1))
 
