@@ -13,3 +13,4 @@ open; its invariants are pinned, its pair layout and base are a reading
 """
 from .attention import *  # noqa: F401,F403
 from .cache import *  # noqa: F401,F403
+from .projection import *  # noqa: F401,F403
