@@ -203,6 +203,21 @@ int32_t ld_split_kv_combine(int32_t num_rows, int32_t d_v, int32_t max_splits, c
 int32_t ld_cache_append(const ld_problem* p, const void* c_new, const void* kr_new, const int32_t* block_table,
                         const int32_t* seq_lens, const ld_kv_cache* cache, float rope_base, void* stream);
 
+/* Per-head projection around the absorbed decode step, bf16 operands, fp32 accumulation:
+ *   c[i, h, j] = sum_{t < k} w[h, j, t] * a[i, h, t]       (i < m, h < heads, j < n)
+ * It is the query absorption, which folds the key up-projection into the query so attention runs in
+ * latent space (a = q^C [B, H, d_nope], w[h] = W_UK[h]^T stored [d_latent, d_nope]), and the output
+ * up-projection that maps the latent result back (a = o_lat [B, H, d_latent], w[h] = W_UV[h]
+ * [d_v, d_latent]); for MLRA, a holds a head's branch outputs side by side [B, H, G*d_latent] and
+ * w[h] the branch up-projections side by side, which sums the branches after projecting them (MLRA
+ * article: the MLA paragraph, and "Moving the Sum Outside"; the "MLA vs MQA" page lists a custom
+ * latent-projection kernel).
+ *   a bf16 [m, heads, k]; w bf16 [heads, n, k] (row j of w[h] holds the k weights of output j);
+ *   c [m, heads, n] in out_dtype (F32 or BF16, rounded to nearest even).  n a multiple of 32, k a
+ *   multiple of 16, pointers 16-byte aligned.  m = 0 does nothing.  Asynchronous on `stream`. */
+int32_t ld_head_projection(int32_t m, int32_t heads, int32_t n, int32_t k, const void* a, const void* w, void* c,
+                           int32_t out_dtype, void* stream);
+
 /* Host check of the metadata: 0 <= seq_lens[b] <= max_pages_per_seq*page_size
  * and every block_table entry a sequence uses lies in [0, num_pages).
  * LD_OK or LD_ERR_BAD_METADATA (or a pointer/shape error). */

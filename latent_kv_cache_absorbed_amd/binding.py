@@ -18,7 +18,7 @@ import torch
 __all__ = [
     "LatentDecodeError", "Decoder", "lib", "library_path", "Problem", "KVCache", "VARIANTS", "DTYPES",
     "make_problem", "workspace_size", "latent_decode", "split_kv_combine", "validate_metadata", "plan_host",
-    "cache_append",
+    "cache_append", "head_projection",
     "check_problem", "status_string", "header_functions",
 ]
 
@@ -82,6 +82,8 @@ def lib():
         L.ld_combine_planned.argtypes = [P, vp, vp, vp, sz, vp]
         L.ld_cache_append.restype = i32
         L.ld_cache_append.argtypes = [P, vp, vp, vp, vp, ctypes.POINTER(KVCache), ctypes.c_float, vp]
+        L.ld_head_projection.restype = i32
+        L.ld_head_projection.argtypes = [i32, i32, i32, i32, vp, vp, vp, i32, vp]
         L.ld_split_kv_combine.restype = i32
         L.ld_split_kv_combine.argtypes = [i32, i32, i32, vp, vp, vp, i32, vp, vp, vp]
         L.ld_validate_metadata.restype = i32
@@ -289,6 +291,26 @@ def cache_append(c_new, kr_new, k, block_table, seq_lens, *, variant: str = "mla
                                ctypes.byref(cache), float(rope_base), ctypes.c_void_p(stream))
     if st:
         raise LatentDecodeError(st, "ld_cache_append")
+
+
+def head_projection(a, w, *, out_dtype: str = "bf16", out=None, stream=None):
+    """ld_head_projection: c[i, h, j] = sum_t w[h, j, t] a[i, h, t]; a bf16 [m, H, k], w bf16 [H, n, k]."""
+    _need(a, "a", (torch.bfloat16,))
+    _need(w, "w", (torch.bfloat16,))
+    m, H, k = a.shape
+    if w.shape[0] != H or w.shape[2] != k:
+        raise ValueError(f"w has shape {tuple(w.shape)}, expected [{H}, n, {k}]")
+    n = w.shape[1]
+    odt = torch.float32 if out_dtype == "f32" else torch.bfloat16
+    if out is None:
+        out = torch.empty((m, H, n), dtype=odt, device=a.device)
+    _need(out, "out", (odt,))
+    if stream is None:
+        stream = torch.cuda.current_stream(a.device).cuda_stream
+    st = lib().ld_head_projection(m, H, n, k, _ptr(a), _ptr(w), _ptr(out), DTYPES[out_dtype], ctypes.c_void_p(stream))
+    if st:
+        raise LatentDecodeError(st, "ld_head_projection")
+    return out
 
 
 def split_kv_combine(partial_out, partial_lse, row_num_splits, *, out_dtype: str = "f32", out=None, lse=None,

@@ -19,7 +19,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "liblatent_decode.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["api.cpp", "plan_combine.hip", "decode.hip", "append.hip"]
+SOURCES = ["api.cpp", "plan_combine.hip", "decode.hip", "append.hip", "projection.hip"]
 
 COMMON = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-I", INCLUDE, "-I", CSRC,
           # packed fp32 VALU forms are kept out of every kernel

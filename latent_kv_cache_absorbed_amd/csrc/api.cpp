@@ -446,6 +446,26 @@ int32_t ld_cache_append(const ld_problem* p, const void* c_new, const void* kr_n
   return launch_append(a, p->kv_dtype, stream) == 0 ? LD_OK : LD_ERR_HIP;
 }
 
+int32_t ld_head_projection(int32_t m, int32_t heads, int32_t n, int32_t k, const void* a, const void* w, void* c,
+                           int32_t out_dtype, void* stream) {
+  if (m < 0 || heads < 1 || n < 32 || n % 32 || k < 16 || k % 16) return LD_ERR_BAD_SHAPE;
+  if ((long long)m * heads * (k > n ? k : n) > (1LL << 40) || (long long)heads * n * k > (1LL << 40))
+    return LD_ERR_BAD_SHAPE;
+  if (out_dtype != LD_F32 && out_dtype != LD_BF16) return LD_ERR_BAD_DTYPE;
+  if (m == 0) return LD_OK;
+  if (!a || !w || !c) return LD_ERR_NULL_POINTER;
+  if (!aligned(a, 16) || !aligned(w, 16) || !aligned(c, 16)) return LD_ERR_MISALIGNED;
+  ProjArgs pa;
+  pa.a = a;
+  pa.w = w;
+  pa.c = c;
+  pa.m = m;
+  pa.heads = heads;
+  pa.n = n;
+  pa.k = k;
+  return launch_head_projection(pa, out_dtype == LD_BF16, stream) == 0 ? LD_OK : LD_ERR_HIP;
+}
+
 int32_t ld_split_kv_combine(int32_t num_rows, int32_t d_v, int32_t max_splits, const float* partial_out,
                             const float* partial_lse, const int32_t* row_num_splits, int32_t out_dtype, void* out,
                             float* lse, void* stream) {

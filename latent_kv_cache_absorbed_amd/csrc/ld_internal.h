@@ -131,6 +131,15 @@ struct AppendArgs {
   float rope_base;
 };
 int launch_append(const AppendArgs& a, int kv_dtype, void* stream);
+
+// per-head projection C[m, h, n] = sum_k W[h, n, k] A[m, h, k] (projection.hip)
+struct ProjArgs {
+  const void* a;   // bf16 [m, heads, k]
+  const void* w;   // bf16 [heads, n, k]
+  void* c;         // [m, heads, n], f32 or bf16
+  int32_t m, heads, n, k;
+};
+int launch_head_projection(const ProjArgs& a, int out_bf16, void* stream);
 // Whether a decode kernel is built for p's dtype/dims/kind with `nsets` sets per work group and
 // `hblocks` 32-head blocks per set.
 bool decode_instantiated(const ld_problem& p, int nsets, int hblocks);

@@ -1,0 +1,98 @@
+// Per-head projections around the absorbed decode step (gfx950): C[m, h, n] = sum_k W[h, n, k] A[m, h, k]
+// with bf16 operands and fp32 accumulation (v_mfma_f32_32x32x16_bf16).  See ld_head_projection in
+// include/latent_decode.h for the operation and its sources.
+//
+// One wave computes a 32-column tile n0 .. n0+31 of one head for every row m, two 32-row tiles at a
+// time.  Both operands are read straight from memory as MFMA fragments: the activation row m holds
+// its K values contiguously and so does the weight row n (W[h] is stored [N, K]), so every lane
+// loads 16 contiguous bytes per k-step.  The weights, which dominate the bytes (H*N*K), are read
+// once per pair of row tiles; the operands of eight k-steps are loaded before their MFMAs issue.
+#include <hip/hip_runtime.h>
+
+#include "decode_common.h"
+#include "ld_internal.h"
+
+namespace ld {
+namespace {
+
+constexpr int kProjThreads = 256;
+constexpr int kKChunk = 8;  // k-steps whose operands are loaded together
+
+__device__ __forceinline__ bf16x8_t load_frag(const __bf16* p) {
+  return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(p));
+}
+
+template <int OUT_BF16>
+__global__ __launch_bounds__(kProjThreads) void head_projection_kernel(ProjArgs a) {
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int ntiles = a.n / 32;
+  const long long gw = (long long)blockIdx.x * (kProjThreads / 64) + wave;
+  if (gw >= (long long)a.heads * ntiles) return;
+  const int h = (int)(gw / ntiles);
+  const int n0 = (int)(gw % ntiles) * 32;
+  const int col = lane & 31;
+  const int hh = lane >> 5;
+  const int ksteps = a.k / 16;
+  const __bf16* A = static_cast<const __bf16*>(a.a);
+  const __bf16* wrow = static_cast<const __bf16*>(a.w) + ((size_t)h * a.n + n0 + col) * a.k + hh * 8;
+  const bf16x8_t zero = __builtin_bit_cast(bf16x8_t, make_uint4(0u, 0u, 0u, 0u));
+  for (int mt = 0; mt < a.m; mt += 64) {
+    const bool two = mt + 32 < a.m;  // wave-uniform: a second row tile
+    const int r0 = mt + col, r1 = mt + 32 + col;
+    const bool v0 = r0 < a.m, v1 = two && r1 < a.m;
+    const __bf16* a0 = A + ((size_t)(v0 ? r0 : 0) * a.heads + h) * a.k + hh * 8;
+    const __bf16* a1 = A + ((size_t)(v1 ? r1 : 0) * a.heads + h) * a.k + hh * 8;
+    floatx16 acc0 = floatx16{}, acc1 = floatx16{};
+    for (int s0 = 0; s0 < ksteps; s0 += kKChunk) {
+      bf16x8_t wf[kKChunk], f0[kKChunk], f1[kKChunk];
+#pragma unroll
+      for (int j = 0; j < kKChunk; ++j) {
+        const int s = min(s0 + j, ksteps - 1);  // steps past the end repeat the last (not used)
+        wf[j] = load_frag(wrow + s * 16);
+        f0[j] = v0 ? load_frag(a0 + s * 16) : zero;
+        f1[j] = v1 ? load_frag(a1 + s * 16) : zero;
+      }
+#pragma unroll
+      for (int j = 0; j < kKChunk; ++j) {
+        if (s0 + j < ksteps) {
+          acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f0[j], wf[j], acc0, 0, 0, 0);
+          if (two) acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f1[j], wf[j], acc1, 0, 0, 0);
+        }
+      }
+    }
+    // lane holds column n0 + col of rows mt + 8 (r / 4) + 4 hh + r % 4 (and 32 further for acc1)
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      if (t == 1 && !two) break;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = mt + 32 * t + 8 * (r >> 2) + 4 * hh + (r & 3);
+        if (m < a.m) {
+          const float v = t == 0 ? acc0[r] : acc1[r];
+          const size_t o = ((size_t)m * a.heads + h) * a.n + n0 + col;
+          if constexpr (OUT_BF16)
+            static_cast<__bf16*>(a.c)[o] = (__bf16)v;
+          else
+            static_cast<float*>(a.c)[o] = v;
+        }
+      }
+    }
+  }
+}
+
+}  // namespace
+
+int launch_head_projection(const ProjArgs& a, int out_bf16, void* stream) {
+  if (a.m == 0) return 0;
+  const long long waves = (long long)a.heads * (a.n / 32);
+  const dim3 grid((unsigned)((waves + kProjThreads / 64 - 1) / (kProjThreads / 64)));
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (out_bf16)
+    hipLaunchKernelGGL(head_projection_kernel<1>, grid, dim3(kProjThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL(head_projection_kernel<0>, grid, dim3(kProjThreads), 0, s, a);
+  return (int)hipGetLastError();
+}
+
+}  // namespace ld

@@ -123,6 +123,18 @@ def test_append_rejects_before_touching_memory():
     assert call(mla(batch=0), c=None, kr=None, bt=None, sl=None) == OK
 
 
+def test_projection_rejects_bad_arguments():
+    L = lkd.lib()
+    g = ctypes.c_void_p(0x10000)
+    assert L.ld_head_projection(4, 2, 48, 32, g, g, g, 1, None) == SHAPE       # n not a multiple of 32
+    assert L.ld_head_projection(4, 2, 64, 40, g, g, g, 1, None) == SHAPE       # k not a multiple of 16
+    assert L.ld_head_projection(4, 0, 64, 32, g, g, g, 1, None) == SHAPE
+    assert L.ld_head_projection(4, 2, 64, 32, g, g, g, 2, None) == DTYPE       # fp8 output
+    assert L.ld_head_projection(4, 2, 64, 32, None, g, g, 1, None) == NULLP
+    assert L.ld_head_projection(4, 2, 64, 32, g, ctypes.c_void_p(0x10008), g, 1, None) == MISAL
+    assert L.ld_head_projection(0, 2, 64, 32, None, None, None, 1, None) == OK
+
+
 def test_workspace_grows_with_forced_splits():
     assert lkd.workspace_size(mla(num_splits=16)) > lkd.workspace_size(mla(num_splits=1))
 
