@@ -287,6 +287,38 @@ def main() -> int:
     plan_ms = timed(lambda i: decs[i % len(decs)].plan())
     dec_ms = timed(lambda i: decs[i % len(decs)].decode())
     comb_ms = timed(lambda i: decs[i % len(decs)].combine())
+    # the cache append of the step's new tokens (the step before the attention), timed on its own
+    # (latent variants): K launches back to back into cache copy 0 (one slot per sequence rewritten)
+    append_ms = None
+    if w.variant in ("mla", "gla", "mlra"):
+        gen = torch.Generator(device=dev).manual_seed(7)
+        c_new = torch.randn((inp.batch, inp.groups * inp.d_lat), generator=gen, device=dev).to(q_lat.dtype)
+        kr_new = torch.randn((inp.batch, inp.d_rope), generator=gen, device=dev).to(q_lat.dtype)
+        k_c, _, r_c, s_c = copies[0]
+        app = lambda i: lkd.cache_append(c_new, kr_new, k_c, bt, sl, variant=w.variant,  # noqa: E731
+                                         groups=inp.groups, rope=r_c, kscale=s_c)
+        app(0)
+        append_ms = timed(app)
+    # the projections around the step (absorbed MLA shapes: d_nope 128, d_v 128, per head): the query
+    # absorption q_lat = W_UK^T q^C and the output up-projection W_UV o_lat, each timed on its own
+    proj = {}
+    if w.variant in ("mla", "gla", "mlra"):
+        gen = torch.Generator(device=dev).manual_seed(8)
+        dn = dv = 128
+        dl = inp.d_lat * (inp.groups if w.variant == "mlra" else 1)     # MLRA: the branches side by side
+        qn = torch.randn((inp.batch, inp.heads, dn), generator=gen, device=dev).to(torch.bfloat16)
+        w_uk_t = (torch.randn((inp.heads, dl, dn), generator=gen, device=dev) * dn ** -0.5).to(torch.bfloat16)
+        ol = torch.randn((inp.batch, inp.heads, dl), generator=gen, device=dev).to(torch.bfloat16)
+        w_uv = (torch.randn((inp.heads, dv, dl), generator=gen, device=dev) * dl ** -0.5).to(torch.bfloat16)
+        for name, (A, W) in {"q_absorb": (qn, w_uk_t), "up_proj": (ol, w_uv)}.items():
+            out_t = torch.empty((A.shape[0], A.shape[1], W.shape[1]), dtype=torch.bfloat16, device=dev)
+            run_p = lambda i, A=A, W=W, o=out_t: lkd.head_projection(A, W, out=o)  # noqa: E731
+            run_p(0)
+            t_ms = timed(run_p)
+            nbytes = (A.numel() + W.numel() + out_t.numel()) * 2
+            proj[name] = {"ms": round(t_ms, 5), "m": A.shape[0], "heads": A.shape[1], "n": W.shape[1], "k": W.shape[2],
+                          "bytes": nbytes, "gbs": round(nbytes / (t_ms * 1e-3) / 1e9, 1),
+                          "hbm_frac": round(nbytes / (t_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
     # single-launch spread of the decode kernel
     one = []
     for i in range(min(K, 20)):
@@ -341,6 +373,7 @@ def main() -> int:
         "kv_tokens_per_s": round(float(lens.sum()) / t, 1),
         "hbm_frac_step": round((kv_bytes + q_bytes + out_bytes) / t / 1e9 / HBM_PEAK_GBS, 4),
         "stage_ms": {"plan": round(plan_ms, 5), "decode": round(dec_ms, 5), "combine": round(comb_ms, 5),
+                     "append": None if append_ms is None else round(append_ms, 5),
                      "decode_single_p10": round(float(np.percentile(one, 10)), 5),
                      "decode_single_p50": round(float(np.percentile(one, 50)), 5),
                      "decode_single_p90": round(float(np.percentile(one, 90)), 5)},
@@ -349,6 +382,7 @@ def main() -> int:
                      "traffic": traffic, "alg_bytes_per_launch": int(dec_alg_bytes),
                      "mfma_tflops": round(mfma_tflops, 2), "mfma_frac": round(mfma_tflops / mfma_peak, 4),
                      "flops_per_launch": int(flops), "decode_source_sha": source_sha()},
+        "projections": proj or None,
         "launch": "hip_graph" if args.graph else "eager",
         "eager_ms_per_step": round(eager_ms / K, 5),
         "input_gen_s": round(gen_s, 2),

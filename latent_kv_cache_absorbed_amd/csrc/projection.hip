@@ -22,62 +22,91 @@ __device__ __forceinline__ bf16x8_t load_frag(const __bf16* p) {
   return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(p));
 }
 
-template <int OUT_BF16>
+// KS waves of a work group share one (head, 32-column tile) and split its k-steps KS ways; with
+// KS = 1 the four waves take four tiles.  Partial sums meet in LDS; the first wave adds them.
+template <int OUT_BF16, int KS>
 __global__ __launch_bounds__(kProjThreads) void head_projection_kernel(ProjArgs a) {
+  constexpr int WAVES = kProjThreads / 64;
+  __shared__ floatx16 part[KS > 1 ? (KS - 1) * 2 * 64 : 1];
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
   const int ntiles = a.n / 32;
-  const long long gw = (long long)blockIdx.x * (kProjThreads / 64) + wave;
-  if (gw >= (long long)a.heads * ntiles) return;
-  const int h = (int)(gw / ntiles);
-  const int n0 = (int)(gw % ntiles) * 32;
+  const long long gw = (long long)blockIdx.x * (WAVES / KS) + wave / KS;   // the tile of this wave
+  const int kq = wave % KS;                                                  // its share of the k-steps
+  const bool live = gw < (long long)a.heads * ntiles;                        // uniform per tile
+  const long long gt = live ? gw : 0;
+  const int h = (int)(gt / ntiles);
+  const int n0 = (int)(gt % ntiles) * 32;
   const int col = lane & 31;
   const int hh = lane >> 5;
   const int ksteps = a.k / 16;
+  const int per = (ksteps + KS - 1) / KS;
+  const int kb = min(kq * per, ksteps), ke = min(kb + per, ksteps);
   const __bf16* A = static_cast<const __bf16*>(a.a);
   const __bf16* wrow = static_cast<const __bf16*>(a.w) + ((size_t)h * a.n + n0 + col) * a.k + hh * 8;
   const bf16x8_t zero = __builtin_bit_cast(bf16x8_t, make_uint4(0u, 0u, 0u, 0u));
   for (int mt = 0; mt < a.m; mt += 64) {
-    const bool two = mt + 32 < a.m;  // wave-uniform: a second row tile
+    const bool two = mt + 32 < a.m;  // uniform: a second row tile
     const int r0 = mt + col, r1 = mt + 32 + col;
     const bool v0 = r0 < a.m, v1 = two && r1 < a.m;
     const __bf16* a0 = A + ((size_t)(v0 ? r0 : 0) * a.heads + h) * a.k + hh * 8;
     const __bf16* a1 = A + ((size_t)(v1 ? r1 : 0) * a.heads + h) * a.k + hh * 8;
     floatx16 acc0 = floatx16{}, acc1 = floatx16{};
-    for (int s0 = 0; s0 < ksteps; s0 += kKChunk) {
-      bf16x8_t wf[kKChunk], f0[kKChunk], f1[kKChunk];
+    if (live) {
+      for (int s0 = kb; s0 < ke; s0 += kKChunk) {
+        bf16x8_t wf[kKChunk], f0[kKChunk], f1[kKChunk];
 #pragma unroll
-      for (int j = 0; j < kKChunk; ++j) {
-        const int s = min(s0 + j, ksteps - 1);  // steps past the end repeat the last (not used)
-        wf[j] = load_frag(wrow + s * 16);
-        f0[j] = v0 ? load_frag(a0 + s * 16) : zero;
-        f1[j] = v1 ? load_frag(a1 + s * 16) : zero;
+        for (int j = 0; j < kKChunk; ++j) {
+          const int s = min(s0 + j, ke - 1);  // steps past the share repeat its last (not used)
+          wf[j] = load_frag(wrow + s * 16);
+          f0[j] = v0 ? load_frag(a0 + s * 16) : zero;
+          f1[j] = v1 ? load_frag(a1 + s * 16) : zero;
+        }
+#pragma unroll
+        for (int j = 0; j < kKChunk; ++j) {
+          if (s0 + j < ke) {
+            acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f0[j], wf[j], acc0, 0, 0, 0);
+            if (two) acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f1[j], wf[j], acc1, 0, 0, 0);
+          }
+        }
       }
+    }
+    if constexpr (KS > 1) {
+      // partial sums of the k shares, added in share order by the tile's first wave; every wave
+      // passes both barriers
+      if (kq > 0) {
+        part[((kq - 1) * 2 + 0) * 64 + lane] = acc0;
+        part[((kq - 1) * 2 + 1) * 64 + lane] = acc1;
+      }
+      __syncthreads();
+      if (kq == 0) {
 #pragma unroll
-      for (int j = 0; j < kKChunk; ++j) {
-        if (s0 + j < ksteps) {
-          acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f0[j], wf[j], acc0, 0, 0, 0);
-          if (two) acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f1[j], wf[j], acc1, 0, 0, 0);
+        for (int q = 1; q < KS; ++q) {
+          acc0 += part[((q - 1) * 2 + 0) * 64 + lane];
+          acc1 += part[((q - 1) * 2 + 1) * 64 + lane];
         }
       }
     }
     // lane holds column n0 + col of rows mt + 8 (r / 4) + 4 hh + r % 4 (and 32 further for acc1)
+    if (live && kq == 0) {
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      if (t == 1 && !two) break;
+      for (int t = 0; t < 2; ++t) {
+        if (t == 1 && !two) break;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int m = mt + 32 * t + 8 * (r >> 2) + 4 * hh + (r & 3);
-        if (m < a.m) {
-          const float v = t == 0 ? acc0[r] : acc1[r];
-          const size_t o = ((size_t)m * a.heads + h) * a.n + n0 + col;
-          if constexpr (OUT_BF16)
-            static_cast<__bf16*>(a.c)[o] = (__bf16)v;
-          else
-            static_cast<float*>(a.c)[o] = v;
+        for (int r = 0; r < 16; ++r) {
+          const int m = mt + 32 * t + 8 * (r >> 2) + 4 * hh + (r & 3);
+          if (m < a.m) {
+            const float v = t == 0 ? acc0[r] : acc1[r];
+            const size_t o = ((size_t)m * a.heads + h) * a.n + n0 + col;
+            if constexpr (OUT_BF16)
+              static_cast<__bf16*>(a.c)[o] = (__bf16)v;
+            else
+              static_cast<float*>(a.c)[o] = v;
+          }
         }
       }
     }
+    if constexpr (KS > 1) __syncthreads();  // the partials are rewritten by the next row tiles
   }
 }
 
@@ -85,13 +114,23 @@ __global__ __launch_bounds__(kProjThreads) void head_projection_kernel(ProjArgs 
 
 int launch_head_projection(const ProjArgs& a, int out_bf16, void* stream) {
   if (a.m == 0) return 0;
-  const long long waves = (long long)a.heads * (a.n / 32);
-  const dim3 grid((unsigned)((waves + kProjThreads / 64 - 1) / (kProjThreads / 64)));
+  constexpr int WAVES = kProjThreads / 64;
+  const long long tiles = (long long)a.heads * (a.n / 32);
+  // a long k is split over the four waves of a work group (one tile each), a short one is not
+  const bool split = a.k / 16 >= 2 * kKChunk;
+  const dim3 grid((unsigned)(split ? tiles : (tiles + WAVES - 1) / WAVES));
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  if (out_bf16)
-    hipLaunchKernelGGL(head_projection_kernel<1>, grid, dim3(kProjThreads), 0, s, a);
-  else
-    hipLaunchKernelGGL(head_projection_kernel<0>, grid, dim3(kProjThreads), 0, s, a);
+  if (split) {
+    if (out_bf16)
+      hipLaunchKernelGGL((head_projection_kernel<1, WAVES>), grid, dim3(kProjThreads), 0, s, a);
+    else
+      hipLaunchKernelGGL((head_projection_kernel<0, WAVES>), grid, dim3(kProjThreads), 0, s, a);
+  } else {
+    if (out_bf16)
+      hipLaunchKernelGGL((head_projection_kernel<1, 1>), grid, dim3(kProjThreads), 0, s, a);
+    else
+      hipLaunchKernelGGL((head_projection_kernel<0, 1>), grid, dim3(kProjThreads), 0, s, a);
+  }
   return (int)hipGetLastError();
 }
 
