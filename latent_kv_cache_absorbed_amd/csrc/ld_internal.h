@@ -21,6 +21,9 @@ constexpr int kWaveSize = 64;
 constexpr int kPlanThreads = 256;
 constexpr int kCombineChunk = 16;     // splits merged by one combine task
 constexpr int kUnitPages = 512;       // pages a work unit spans at most (its block-table entries fit in LDS)
+// Batches of at most this many sequences are combined by one launch of wide work groups (each
+// sequence then has many splits); larger batches by per-task work groups and a chunk merge.
+constexpr int kSeqCombineMaxBatch = 8;
 
 // Work unit record written by the planner: one (sequence, token chunk).
 struct alignas(16) Unit {

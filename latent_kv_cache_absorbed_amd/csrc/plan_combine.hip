@@ -282,6 +282,17 @@ struct Merge {
     }
     M = Mn;
   }
+  // fold in another state (its pairs come after this one's)
+  __device__ __forceinline__ void merge(float M2, float tot2, const float* o2) {
+    const float Mn = fmaxf(M, M2);
+    if (Mn == -INFINITY) return;
+    const float r1 = (M == -INFINITY) ? 0.f : expf(M - Mn);
+    const float r2 = (M2 == -INFINITY) ? 0.f : expf(M2 - Mn);
+    tot = tot * r1 + tot2 * r2;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = o[e] * r1 + o2[e] * r2;
+    M = Mn;
+  }
   // normalised output and lse (0 and -inf when every lse was -inf)
   __device__ __forceinline__ float finish() {
     if (M == -INFINITY) return -INFINITY;
@@ -392,6 +403,65 @@ __global__ __launch_bounds__(kCombineThreads) void combine_ws_kernel(DecodeArgs 
   a.l2_lse[lo] = lse;
 }
 
+// Batches of a few long sequences (many splits each): work group (x, b) merges piece group x of
+// sequence b in one launch.  Its kSeqWaves waves take the sequence's chunks of kCombineChunk splits
+// round-robin, each folding them into its own running state; the states then meet in LDS and the
+// first wave folds them in wave order and writes the result.
+constexpr int kSeqWaves = 16;
+
+__global__ __launch_bounds__(kSeqWaves * 64) void combine_seq_kernel(DecodeArgs a, int d_v) {
+  __shared__ float st_m[kSeqWaves][64], st_t[kSeqWaves][64], st_o[kSeqWaves][8][64];
+  const int b = blockIdx.y;
+  const int n_all = a.seqs[4 * b];
+  if (n_all == 1) return;  // the decode kernel wrote this sequence's output
+  const int first = a.seqs[4 * b + 1];
+  const int n = max(0, min(n_all, a.max_units - first));
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const PieceGroup p = piece_group(a, d_v, blockIdx.x);
+  const int vals = a.part_bf16 ? 8 : 4;
+  Merge m;
+  for (int c0 = wave * kCombineChunk; c0 < n; c0 += kSeqWaves * kCombineChunk) {
+    const int cnt = min(n - c0, kCombineChunk);
+    for (int k0 = 0; k0 < cnt; k0 += kBatch) {
+      float ls[kBatch], v[kBatch][8];
+#pragma unroll
+      for (int k = 0; k < kBatch; ++k) {
+        const size_t s = first + c0 + min(k0 + k, cnt - 1);
+        ls[k] = a.part_lse[(s * p.blocks_per_unit + p.blk_in_unit) * 32 + (lane & 31)];
+        const size_t off = (s * p.blocks_per_unit + p.blk_in_unit) * (size_t)(32 * d_v) + p.piece_off;
+        if (a.part_bf16) {
+          typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+          const bf16x8_t x = *reinterpret_cast<const bf16x8_t*>(static_cast<const __bf16*>(a.part_out) + off);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[k][e] = (float)x[e];
+        } else {
+          const float4 x = *reinterpret_cast<const float4*>(static_cast<const float*>(a.part_out) + off);
+          v[k][0] = x.x, v[k][1] = x.y, v[k][2] = x.z, v[k][3] = x.w;
+          v[k][4] = v[k][5] = v[k][6] = v[k][7] = 0.f;
+        }
+      }
+      m.add(ls, v, cnt - k0, vals);
+    }
+  }
+  st_m[wave][lane] = m.M;
+  st_t[wave][lane] = m.tot;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) st_o[wave][e][lane] = m.o[e];
+  __syncthreads();
+  if (wave != 0) return;
+  // wave w's chunks are w, w + kSeqWaves, ...: folding the states in wave order is not split order,
+  // but the merge is a sum, so only the rounding differs
+  for (int w = 1; w < kSeqWaves; ++w) {
+    float o2[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o2[e] = st_o[w][e][lane];
+    m.merge(st_m[w][lane], st_t[w][lane], o2);
+  }
+  const float lse = m.finish();
+  write_piece(a, d_v, p, b, m.o, lse);
+}
+
 // Merge the chunk results of the sequences combined in more than one chunk, in chunk order.  The
 // grid's second dimension strides over those sequences.
 __global__ __launch_bounds__(kCombineThreads) void combine_chunks_kernel(DecodeArgs a, int d_v) {
@@ -472,6 +542,13 @@ int launch_plan(const PlanArgs& a, void* stream) {
 
 int launch_combine_ws(const DecodeArgs& a, int32_t d_v, void* stream) {
   if (a.batch == 0 || a.rows == 0) return 0;
+  if (a.batch <= kSeqCombineMaxBatch) {
+    // a few sequences, so (when split) many splits each: one launch, one wide work group per
+    // (piece group, sequence)
+    hipLaunchKernelGGL(combine_seq_kernel, dim3(a.xblocks * 4, a.batch), dim3(kSeqWaves * 64), 0,
+                       static_cast<hipStream_t>(stream), a, d_v);
+    return (int)hipGetLastError();
+  }
   hipLaunchKernelGGL(combine_ws_kernel, dim3(a.xblocks, a.max_tasks), dim3(kCombineThreads), 0,
                      static_cast<hipStream_t>(stream), a, d_v);
   int r = (int)hipGetLastError();
