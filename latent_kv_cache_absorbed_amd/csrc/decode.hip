@@ -117,13 +117,19 @@ __global__ __launch_bounds__(NSETS* HB* SPLIT * 64) void decode_kernel(DecodeArg
   __shared__ __attribute__((aligned(16))) float lds_exch[C::EXCH / 4];
   __shared__ int lds_pages[kUnitPages];
 
-  // XCD-aware mapping: all work groups of one unit land on the same XCD (ids = unit mod 8)
+  // XCD-aware mapping: work groups are dealt to the 8 XCDs round-robin, so blockIdx mod 8 names
+  // the XCD.  All work groups of one unit land on one XCD, and XCD k takes the consecutive units
+  // [k*per, (k+1)*per): the splits of one sequence share an L2, which fetches its query once.
   const int x = blockIdx.x;
   const int xcd = x & 7;
   const int y = x >> 3;
   const int sb = y % a.wg_per_unit;
-  const int unit = (y / a.wg_per_unit) * 8 + xcd;
-  if (unit >= a.header[0]) return;
+  const int nunits = a.header[0];
+  const int per = (nunits + 7) >> 3;
+  const int yy = y / a.wg_per_unit;
+  if (yy >= per) return;
+  const int unit = xcd * per + yy;
+  if (unit >= nunits) return;
   const Unit u = a.units[unit];
   const int b = u.b;
   const int t_begin = u.t_begin;
