@@ -258,6 +258,10 @@ __device__ __forceinline__ void write_piece(const DecodeArgs& a, int d_v, const 
 // sum and weighted values are updated.  Pairs are taken in index order.
 constexpr int kBatch = 8;
 
+// e^x for merge weights (x <= 0): v_exp_f32 of x log2(e); the relative error of a weight is below
+// 2^-22 (1 + |x|), and weights of large |x| are negligible beside the largest (which is 1)
+__device__ __forceinline__ float wexp(float x) { return __builtin_amdgcn_exp2f(x * 1.44269504088896340736f); }
+
 struct Merge {
   float M = -INFINITY, tot = 0.f, o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   template <int KB = kBatch>
@@ -268,13 +272,13 @@ struct Merge {
       if (k < valid) bm = fmaxf(bm, ls[k]);
     const float Mn = fmaxf(M, bm);
     if (Mn == -INFINITY) return;
-    const float r = (M == -INFINITY) ? 0.f : expf(M - Mn);
+    const float r = (M == -INFINITY) ? 0.f : wexp(M - Mn);
     tot *= r;
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[e] *= r;
 #pragma unroll
     for (int k = 0; k < KB; ++k) {
-      const float w = k < valid ? expf(ls[k] - Mn) : 0.f;
+      const float w = k < valid ? wexp(ls[k] - Mn) : 0.f;
       tot += w;
 #pragma unroll
       for (int e = 0; e < 8; ++e)
@@ -286,8 +290,8 @@ struct Merge {
   __device__ __forceinline__ void merge(float M2, float tot2, const float* o2) {
     const float Mn = fmaxf(M, M2);
     if (Mn == -INFINITY) return;
-    const float r1 = (M == -INFINITY) ? 0.f : expf(M - Mn);
-    const float r2 = (M2 == -INFINITY) ? 0.f : expf(M2 - Mn);
+    const float r1 = (M == -INFINITY) ? 0.f : wexp(M - Mn);
+    const float r2 = (M2 == -INFINITY) ? 0.f : wexp(M2 - Mn);
     tot = tot * r1 + tot2 * r2;
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[e] = o[e] * r1 + o2[e] * r2;
@@ -405,8 +409,9 @@ __global__ __launch_bounds__(kCombineThreads) void combine_ws_kernel(DecodeArgs 
 
 // Batches of a few long sequences (many splits each): work group (x, b) merges piece group x of
 // sequence b in one launch.  Its kSeqWaves waves take the sequence's chunks of kCombineChunk splits
-// round-robin, each folding them into its own running state; the states then meet in LDS and the
-// first wave folds them in wave order and writes the result.
+// round-robin; a wave issues all loads of a chunk at once and folds the chunk into its running
+// state in one step.  The states then meet in LDS in two rounds (four waves fold four states each,
+// then the first wave folds those four) and the first wave writes the result.
 constexpr int kSeqWaves = 16;
 
 __global__ __launch_bounds__(kSeqWaves * 64) void combine_seq_kernel(DecodeArgs a, int d_v) {
@@ -419,29 +424,49 @@ __global__ __launch_bounds__(kSeqWaves * 64) void combine_seq_kernel(DecodeArgs 
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
   const PieceGroup p = piece_group(a, d_v, blockIdx.x);
-  const int vals = a.part_bf16 ? 8 : 4;
   Merge m;
   for (int c0 = wave * kCombineChunk; c0 < n; c0 += kSeqWaves * kCombineChunk) {
     const int cnt = min(n - c0, kCombineChunk);
-    for (int k0 = 0; k0 < cnt; k0 += kBatch) {
-      float ls[kBatch], v[kBatch][8];
+    // every load of the chunk is issued before any is used (raw pieces: 16 bytes each)
+    float ls[kCombineChunk];
+    uint4 raw[kCombineChunk];
 #pragma unroll
-      for (int k = 0; k < kBatch; ++k) {
-        const size_t s = first + c0 + min(k0 + k, cnt - 1);
-        ls[k] = a.part_lse[(s * p.blocks_per_unit + p.blk_in_unit) * 32 + (lane & 31)];
-        const size_t off = (s * p.blocks_per_unit + p.blk_in_unit) * (size_t)(32 * d_v) + p.piece_off;
+    for (int k = 0; k < kCombineChunk; ++k) {
+      const size_t s = first + c0 + min(k, cnt - 1);
+      ls[k] = a.part_lse[(s * p.blocks_per_unit + p.blk_in_unit) * 32 + (lane & 31)];
+      const size_t off = (s * p.blocks_per_unit + p.blk_in_unit) * (size_t)(32 * d_v) + p.piece_off;
+      raw[k] = a.part_bf16 ? *reinterpret_cast<const uint4*>(static_cast<const __bf16*>(a.part_out) + off)
+                           : *reinterpret_cast<const uint4*>(static_cast<const float*>(a.part_out) + off);
+    }
+    // one online-merge step over the whole chunk, each piece converted as it is folded in
+    float bm = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < kCombineChunk; ++k)
+      if (k < cnt) bm = fmaxf(bm, ls[k]);
+    const float Mn = fmaxf(m.M, bm);
+    if (Mn != -INFINITY) {
+      const float r = (m.M == -INFINITY) ? 0.f : wexp(m.M - Mn);
+      m.tot *= r;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) m.o[e] *= r;
+#pragma unroll
+      for (int k = 0; k < kCombineChunk; ++k) {
+        const float w = k < cnt ? wexp(ls[k] - Mn) : 0.f;
+        m.tot += w;
+        const uint4 x = raw[k];
         if (a.part_bf16) {
           typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-          const bf16x8_t x = *reinterpret_cast<const bf16x8_t*>(static_cast<const __bf16*>(a.part_out) + off);
+          const bf16x8_t y = __builtin_bit_cast(bf16x8_t, x);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) v[k][e] = (float)x[e];
+          for (int e = 0; e < 8; ++e) m.o[e] += w * (float)y[e];
         } else {
-          const float4 x = *reinterpret_cast<const float4*>(static_cast<const float*>(a.part_out) + off);
-          v[k][0] = x.x, v[k][1] = x.y, v[k][2] = x.z, v[k][3] = x.w;
-          v[k][4] = v[k][5] = v[k][6] = v[k][7] = 0.f;
+          m.o[0] += w * __builtin_bit_cast(float, x.x);
+          m.o[1] += w * __builtin_bit_cast(float, x.y);
+          m.o[2] += w * __builtin_bit_cast(float, x.z);
+          m.o[3] += w * __builtin_bit_cast(float, x.w);
         }
       }
-      m.add(ls, v, cnt - k0, vals);
+      m.M = Mn;
     }
   }
   st_m[wave][lane] = m.M;
@@ -449,15 +474,32 @@ __global__ __launch_bounds__(kSeqWaves * 64) void combine_seq_kernel(DecodeArgs 
 #pragma unroll
   for (int e = 0; e < 8; ++e) st_o[wave][e][lane] = m.o[e];
   __syncthreads();
-  if (wave != 0) return;
-  // wave w's chunks are w, w + kSeqWaves, ...: folding the states in wave order is not split order,
-  // but the merge is a sum, so only the rounding differs
-  for (int w = 1; w < kSeqWaves; ++w) {
+  // the states meet in two rounds: waves 0..3 fold in waves w + 4, w + 8, w + 12, then wave 0 folds
+  // in waves 1..3 (wave w's chunks are w, w + kSeqWaves, ...; the merge is a sum, so the order
+  // changes only the rounding)
+  auto fold = [&](int w) {
     float o2[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) o2[e] = st_o[w][e][lane];
     m.merge(st_m[w][lane], st_t[w][lane], o2);
+  };
+  if (wave < 4) {
+    fold(wave + 4);
+    fold(wave + 8);
+    fold(wave + 12);
   }
+  __syncthreads();
+  if (wave >= 1 && wave < 4) {
+    st_m[wave][lane] = m.M;
+    st_t[wave][lane] = m.tot;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) st_o[wave][e][lane] = m.o[e];
+  }
+  __syncthreads();
+  if (wave != 0) return;
+  fold(1);
+  fold(2);
+  fold(3);
   const float lse = m.finish();
   write_piece(a, d_v, p, b, m.o, lse);
 }
