@@ -310,19 +310,7 @@ DecodeArgs decode_args(const ld_problem* p, const WsLayout& w, void* workspace) 
   return a;
 }
 
-}  // namespace
-
-extern "C" {
-
-int32_t ld_plan(const ld_problem* p, const int32_t* seq_lens, void* workspace, size_t workspace_bytes, void* stream) {
-  const int32_t st = ld_check_problem(p);
-  if (st != LD_OK) return st;
-  if (p->batch == 0) return LD_OK;
-  if (!seq_lens) return LD_ERR_NULL_POINTER;
-  if (!aligned(seq_lens, 4)) return LD_ERR_MISALIGNED;
-  WsLayout w;
-  const int32_t sw = check_workspace(p, workspace, workspace_bytes, &w);
-  if (sw != LD_OK) return sw;
+PlanArgs plan_args(const ld_problem* p, const WsLayout& w, void* workspace, const int32_t* seq_lens) {
   char* ws = static_cast<char*>(workspace);
   PlanArgs pa;
   pa.seq_lens = seq_lens;
@@ -339,7 +327,46 @@ int32_t ld_plan(const ld_problem* p, const int32_t* seq_lens, void* workspace, s
   pa.target_units = target_units_for(*p, device_cu_count());
   pa.forced_splits = p->num_splits;
   pa.max_units = w.max_units;
-  return launch_plan(pa, stream) == hipSuccess ? LD_OK : LD_ERR_HIP;
+  return pa;
+}
+
+// The decode launch shared by ld_decode_planned (plan read from the workspace) and
+// ld_latent_decode (plan derived in the kernel, fused = true).
+int32_t decode_launch(const ld_problem* p, const WsLayout& w, const void* q_latent, const void* q_rope,
+                      const ld_kv_cache* cache, const int32_t* block_table, const int32_t* seq_lens, void* out,
+                      float* lse, void* workspace, bool fused, void* stream) {
+  DecodeArgs a = decode_args(p, w, workspace);
+  a.q_lat = q_latent;
+  a.q_rope = q_rope;
+  a.k = cache->k;
+  a.rope = cache->rope;
+  a.v = cache->v;
+  a.kscale = cache->scale;
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  a.out = out;
+  a.lse = lse;
+  a.fused_plan = fused ? 1 : 0;
+  if (fused) a.plan = plan_args(p, w, workspace, seq_lens);
+  const int r = launch_decode(*p, a, stream);
+  if (r == -1) return LD_ERR_UNSUPPORTED;
+  return r == hipSuccess ? LD_OK : LD_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t ld_plan(const ld_problem* p, const int32_t* seq_lens, void* workspace, size_t workspace_bytes, void* stream) {
+  const int32_t st = ld_check_problem(p);
+  if (st != LD_OK) return st;
+  if (p->batch == 0) return LD_OK;
+  if (!seq_lens) return LD_ERR_NULL_POINTER;
+  if (!aligned(seq_lens, 4)) return LD_ERR_MISALIGNED;
+  WsLayout w;
+  const int32_t sw = check_workspace(p, workspace, workspace_bytes, &w);
+  if (sw != LD_OK) return sw;
+  return launch_plan(plan_args(p, w, workspace, seq_lens), stream) == hipSuccess ? LD_OK : LD_ERR_HIP;
 }
 
 int32_t ld_decode_planned(const ld_problem* p, const void* q_latent, const void* q_rope, const ld_kv_cache* cache,
@@ -353,20 +380,7 @@ int32_t ld_decode_planned(const ld_problem* p, const void* q_latent, const void*
   WsLayout w;
   const int32_t sw = check_workspace(p, workspace, workspace_bytes, &w);
   if (sw != LD_OK) return sw;
-  DecodeArgs a = decode_args(p, w, workspace);
-  a.q_lat = q_latent;
-  a.q_rope = q_rope;
-  a.k = cache->k;
-  a.rope = cache->rope;
-  a.v = cache->v;
-  a.kscale = cache->scale;
-  a.block_table = block_table;
-  a.seq_lens = seq_lens;
-  a.out = out;
-  a.lse = lse;
-  const int r = launch_decode(*p, a, stream);
-  if (r == -1) return LD_ERR_UNSUPPORTED;
-  return r == hipSuccess ? LD_OK : LD_ERR_HIP;
+  return decode_launch(p, w, q_latent, q_rope, cache, block_table, seq_lens, out, lse, workspace, false, stream);
 }
 
 int32_t ld_combine_planned(const ld_problem* p, void* out, float* lse, void* workspace, size_t workspace_bytes,
@@ -396,10 +410,10 @@ int32_t ld_latent_decode(const ld_problem* p, const void* q_latent, const void* 
   WsLayout w;
   const int32_t sw = check_workspace(p, workspace, workspace_bytes, &w);
   if (sw != LD_OK) return sw;
-  int32_t r = ld_plan(p, seq_lens, workspace, workspace_bytes, stream);
-  if (r != LD_OK) return r;
-  r = ld_decode_planned(p, q_latent, q_rope, cache, block_table, seq_lens, out, lse, workspace, workspace_bytes,
-                        stream);
+  // one launch fewer than ld_plan + ld_decode_planned: the decode kernel plans for itself and
+  // leaves the plan arrays in the workspace for the combine
+  const int32_t r = decode_launch(p, w, q_latent, q_rope, cache, block_table, seq_lens, out, lse, workspace, true,
+                                  stream);
   if (r != LD_OK) return r;
   return ld_combine_planned(p, out, lse, workspace, workspace_bytes, stream);
 }

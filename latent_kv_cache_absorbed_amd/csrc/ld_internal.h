@@ -56,6 +56,24 @@ struct WsLayout {
   size_t total = 0;
 };
 
+// Planner inputs and the plan arrays it writes (ld_plan, or the decode kernel's fused prologue).
+struct PlanArgs {
+  const int32_t* seq_lens;
+  int32_t* header;
+  Unit* units;
+  int32_t* seqs;
+  int32_t* tasks;
+  int32_t* multi;
+  int32_t max_tasks;
+  int32_t max_multi;
+  int32_t batch;
+  int32_t capacity;       // max_pages_per_seq * page_size
+  int32_t page_size;
+  int32_t target_units;   // units the planner aims for (auto mode)
+  int32_t forced_splits;  // 0 = auto
+  int32_t max_units;
+};
+
 // Everything the decode kernels need, passed by value.
 struct DecodeArgs {
   const void* q_lat;
@@ -86,24 +104,13 @@ struct DecodeArgs {
   int32_t part_bf16;            // partials stored as bf16 (else f32)
   int32_t mlra;
   float scale_log2;             // softmax_scale * log2(e)
+  // Fused plan (ld_latent_decode): every work group derives its unit from seq_lens with the
+  // planner rule instead of reading the plan arrays, and the work groups write those arrays for
+  // the combine (plan.* pointers).
+  int32_t fused_plan;
+  PlanArgs plan;
 };
 
-struct PlanArgs {
-  const int32_t* seq_lens;
-  int32_t* header;
-  Unit* units;
-  int32_t* seqs;
-  int32_t* tasks;
-  int32_t* multi;
-  int32_t max_tasks;
-  int32_t max_multi;
-  int32_t batch;
-  int32_t capacity;       // max_pages_per_seq * page_size
-  int32_t page_size;
-  int32_t target_units;   // units the planner aims for (auto mode)
-  int32_t forced_splits;  // 0 = auto
-  int32_t max_units;
-};
 
 // Host planner rule shared (as a specification, not as code) with the device
 // planner: see plan_chunk() in api.cpp and plan_kernel in plan_combine.hip.

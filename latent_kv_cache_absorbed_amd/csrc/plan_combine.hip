@@ -1,13 +1,7 @@
 // Split-KV planner and log-sum-exp combine kernels (gfx950).
 //
-// Planner rule (identical to plan_host in api.cpp, which tests compare against):
-//   L_b   = clamp(seq_lens[b], 0, capacity)
-//   auto:   chunk = the smallest multiple of page with sum_b ceil(L_b / chunk) <= target_units
-//           (roundup(max_b L_b, page) when none is);                          n_b = ceil(L_b / chunk)
-//   forced: chunk_b = max(page, roundup(ceil(L_b / splits), page));        n_b = ceil(L_b / chunk_b)
-//   either chunk is capped at kUnitPages pages
-//   units of sequence b are first_b .. first_b + n_b - 1 (first_b = exclusive prefix sum of n_b),
-//   unit first_b + s covers tokens [s * chunk_b, min(L_b, (s + 1) * chunk_b)).
+// The planner rule is stated in plan_common.h (identical to plan_host in api.cpp, which tests
+// compare against).
 //
 // Combine rule for a row split into n parts with normalised partial outputs o_s and
 // log-sum-exps lse_s:  lse = ln sum_s exp(lse_s),  o = sum_s exp(lse_s - lse) o_s.
@@ -16,6 +10,7 @@
 #include <type_traits>
 
 #include "ld_internal.h"
+#include "plan_common.h"
 
 namespace ld {
 namespace {
@@ -23,7 +18,6 @@ namespace {
 __device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
 
 constexpr int kOwnUnits = 8;
-constexpr int kCachedLens = 16;  // page counts per lane of the searching wave kept in registers
 
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   __shared__ int scan[kPlanThreads];
@@ -37,87 +31,26 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   __shared__ int long_b[kPlanThreads], long_n[kPlanThreads], long_first[kPlanThreads], long_L[kPlanThreads],
       long_ck[kPlanThreads];
   const int tid = threadIdx.x;
-  const int page = a.page_size;
 
-  // auto: the smallest chunk (a multiple of the page) that splits the batch into at most
-  // target_units units, found by bisection on the page count (the unit count only falls as the
-  // chunk grows; ceil(L / (k * page)) = ceil(ceil(L / page) / k)); the longest length when even
-  // one unit per sequence is more than that.  Wave 0 searches alone, with the page counts of the
-  // first 64 * kCachedLens sequences in registers.
   if (tid == 0) {
     s_carry = 0;
     s_carry2 = 0;
     s_carry3 = 0;
     s_chunk = 0;
   }
-  if (a.forced_splits <= 0 && tid < 64) {
-    auto pages_of = [&](int b) { return (unsigned)((clampi(a.seq_lens[b], 0, a.capacity) + page - 1) / page); };
-    unsigned pg[kCachedLens];
-    unsigned mx = 0, sum = 0;
-    const int kk = min(kCachedLens, (a.batch + 63) / 64);  // cached rows in use (uniform)
-#pragma unroll
-    for (int k = 0; k < kCachedLens; ++k) {
-      const int b = tid + 64 * k;
-      pg[k] = (k < kk && b < a.batch) ? pages_of(b) : 0u;
-      mx = max(mx, pg[k]);
-      sum = min(sum + pg[k], 1u << 30);
-    }
-    for (int b = tid + 64 * kCachedLens; b < a.batch; b += 64) {
-      const unsigned pb = pages_of(b);
-      mx = max(mx, pb);
-      sum = min(sum + pb, 1u << 30);
-    }
-    for (int off = 32; off > 0; off >>= 1) {
-      mx = max(mx, (unsigned)__shfl_xor((int)mx, off));
-      sum = min(sum + (unsigned)__shfl_xor((int)sum, off), 1u << 30);
-    }
-    auto count = [&](unsigned k) {  // units for a chunk of k pages, saturated at 2^30
-      unsigned cnt = 0;
-#pragma unroll
-      for (int j = 0; j < kCachedLens; ++j)
-        if (j < kk) cnt += (pg[j] + k - 1) / k;
-      for (int b = tid + 64 * kCachedLens; b < a.batch; b += 64) cnt = min(cnt + (pages_of(b) + k - 1) / k, 1u << 30);
-      for (int off = 32; off > 0; off >>= 1) cnt = min(cnt + (unsigned)__shfl_xor((int)cnt, off), 1u << 30);
-      return cnt;
-    };
-    // sum_b ceil(P_b / k) >= sum_b P_b / k, so no k below ceil(sum / target) qualifies; for
-    // balanced lengths that bound usually does
-    const unsigned tu = (unsigned)a.target_units;
-    unsigned lo = max(1u, (sum + tu - 1) / tu), hi = max(mx, 1u);
-    if (lo >= hi || count(lo) <= tu) {
-      hi = lo = min(lo, hi);
-    } else {
-      lo = lo + 1;
-    }
-    while (lo < hi) {  // uniform across the wave
-      const unsigned mid = (lo + hi) >> 1;
-      if (count(mid) <= tu)
-        hi = mid;
-      else
-        lo = mid + 1;
-    }
-    if (tid == 0) s_chunk = (int)min(lo, (unsigned)kUnitPages) * page;
+  if (tid < 64) {
+    const int c = plan_auto_chunk(a, tid);
+    if (tid == 0) s_chunk = c;
   }
   __syncthreads();
   const int chunk = s_chunk;
 
   for (int base = 0; base < a.batch; base += blockDim.x) {
     const int b = base + tid;
-    int L = 0, ck = chunk, n = 0;
-    if (b < a.batch) {
-      L = clampi(a.seq_lens[b], 0, a.capacity);
-      if (a.forced_splits > 0) {
-        const int per = (L + a.forced_splits - 1) / a.forced_splits;
-        ck = (per + page - 1) / page * page;
-        if (ck < page) ck = page;
-        if (ck > kUnitPages * page) ck = kUnitPages * page;
-      }
-      n = (L + ck - 1) / ck;
-    }
     // combine tasks of this sequence: none for one split (the decode kernel writes the output),
     // one for an empty sequence (it writes zeros), else one per chunk of kCombineChunk splits
-    const int nc = (b >= a.batch || n == 1) ? 0 : (n == 0 ? 1 : (n + kCombineChunk - 1) / kCombineChunk);
-    const int mc = nc > 1 ? 1 : 0;
+    const SeqPlan sp = plan_seq(a, chunk, b);
+    const int L = sp.L, ck = sp.ck, n = sp.n, nc = sp.nc, mc = sp.mc;
     scan[tid] = n;
     scan2[tid] = nc;
     scan3[tid] = mc;

@@ -166,6 +166,47 @@ def test_mla_bf16_forced_many_splits(splits):
     _check(inp, num_splits=splits)
 
 
+# --- ld_latent_decode derives the split plan inside the decode kernel (and leaves the plan arrays
+# for the combine); ld_plan + ld_decode_planned + ld_combine_planned read it from the workspace.
+# Same planner rule, same kernels: the two give the same bits.  Cases cover empty sequences, an
+# all-empty batch, forced splits, a batch above the one-launch combine limit with a sequence merged
+# in several chunks, and two work groups per unit (MLRA-4: two branches per work group).
+_S = 1 / math.sqrt(192)
+
+
+@pytest.mark.parametrize("variant,H,G,d,dr,lens,splits,kv", [
+    ("mla", 128, 1, 512, 64, [0, 70, 0, 4097, 1], 0, "bf16"),
+    ("mla", 128, 1, 512, 64, [0, 0], 0, "bf16"),
+    ("mla", 128, 1, 512, 64, [5000, 64, 2600], 9, "bf16"),
+    ("mla", 128, 1, 512, 64, [1500, 700], 1, "bf16"),
+    ("mla", 128, 1, 512, 64, [40000] + [300 + 97 * i for i in range(9)], 0, "bf16"),
+    ("mlra", 128, 4, 128, 64, [700, 33, 2500], 0, "bf16"),
+    ("gla", 128, 2, 256, 64, [1, 500, 1111], 0, "fp8_e4m3"),
+])
+def test_fused_plan_matches_staged_plan(variant, H, G, d, dr, lens, splits, kv):
+    import latent_kv_cache_absorbed_amd as lkd
+    from gpu_util import to_dev
+    inp = synth.make_inputs(variant, len(lens), H, G, d, dr, lens, scale=_S, seed=31, kv_dtype=kv)
+    print(f"case fused vs staged plan {variant} lens={lens} splits={splits} kv={kv}", flush=True)
+    bt = torch.from_numpy(inp.layout.block_table).cuda()
+    sl = torch.from_numpy(inp.layout.seq_lens).cuda()
+    mk = lambda: lkd.Decoder(to_dev(inp.q_lat), to_dev(inp.q_rope), to_dev(inp.k_pool), bt, sl,  # noqa: E731
+                             variant=variant, scale=inp.scale, groups=G, rope=to_dev(inp.rope_pool),
+                             kscale=to_dev(inp.scale_pool), num_splits=splits)
+    fused, staged = mk(), mk()
+    for d_ in (fused, staged):
+        d_.out.fill_(float("nan"))
+        d_.lse.fill_(float("nan"))
+        d_.workspace.fill_(0xFF)
+    fused.run()
+    staged.plan()
+    staged.decode()
+    staged.combine()
+    torch.cuda.synchronize()
+    assert torch.equal(fused.out, staged.out) and torch.equal(fused.lse, staged.lse)
+    assert not torch.isnan(fused.out).any()
+
+
 # --- the whole step (plan + decode + one- and two-level combine) captured in a HIP graph: every
 # replay, with eager work on the same buffers in between, reproduces the eager result bit for bit
 @pytest.mark.parametrize("lens", [[1500, 77, 3000], [40000]])
