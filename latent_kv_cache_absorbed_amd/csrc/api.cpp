@@ -72,6 +72,8 @@ WsLayout ws_layout(const ld_problem& p, int num_cus) {
   off = round256(off + (size_t)w.max_tasks * pieces * vals * sizeof(float));
   w.l2_lse = off;
   off = round256(off + (size_t)w.max_tasks * pieces * sizeof(float));
+  w.ccount = off;
+  off = round256(off + (size_t)w.max_tasks * w.xblocks * sizeof(int32_t));
   w.total = off;
   return w;
 }
@@ -288,6 +290,7 @@ DecodeArgs decode_args(const ld_problem* p, const WsLayout& w, void* workspace) 
   a.multi = reinterpret_cast<const int32_t*>(ws + w.multi);
   a.l2_out = reinterpret_cast<float*>(ws + w.l2_out);
   a.l2_lse = reinterpret_cast<float*>(ws + w.l2_lse);
+  a.ccount = reinterpret_cast<int32_t*>(ws + w.ccount);
   a.max_tasks = w.max_tasks;
   a.max_multi = w.max_multi;
   a.xblocks = w.xblocks;
@@ -319,6 +322,8 @@ PlanArgs plan_args(const ld_problem* p, const WsLayout& w, void* workspace, cons
   pa.seqs = reinterpret_cast<int32_t*>(ws + w.seqs);
   pa.tasks = reinterpret_cast<int32_t*>(ws + w.tasks);
   pa.multi = reinterpret_cast<int32_t*>(ws + w.multi);
+  pa.ccount = reinterpret_cast<int32_t*>(ws + w.ccount);
+  pa.ccount_n = w.max_tasks * w.xblocks;
   pa.max_tasks = w.max_tasks;
   pa.max_multi = w.max_multi;
   pa.batch = p->batch;

@@ -104,7 +104,8 @@ struct Cfg {
 // plan), then that unit's sequence, split and token range, which it leaves in u[0..4] (u[0] = -1:
 // no unit).  The plan arrays the combine reads are written on the way: each sequence's entries and
 // tasks by the first work group of its first unit, the unit record by the unit's first work group,
-// and the header plus the entries of empty sequences (which have no unit) by work group 0.
+// and the header, the entries of empty sequences (which have no unit) and the zeroed combine
+// arrival counters by work group 0.
 __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
@@ -156,6 +157,7 @@ __device__ __forceinline__ void fused_plan_unit(const DecodeArgs& a, int x, int 
       P.header[2] = min(tc, P.max_tasks);
       P.header[3] = min(tm, P.max_multi);
     }
+    for (int i = lane; i < P.ccount_n; i += 64) P.ccount[i] = 0;  // combine arrival counters
     // empty sequences: one combine task each, which writes zeros
     int cn = 0, cc = 0;
     for (int base = 0; base < P.batch; base += 64) {

@@ -48,6 +48,7 @@ struct WsLayout {
   size_t multi = 0;        // int32[max_multi]: sequences merged in more than one chunk
   size_t l2_out = 0;       // f32[max_tasks][pieces][values]: chunk results of multi-chunk sequences
   size_t l2_lse = 0;       // f32[max_tasks][pieces]: their lse, per piece lane
+  size_t ccount = 0;       // int32[max_tasks][xblocks]: arrivals of a sequence's chunk tasks (first task's row)
   // Split partials, one slot per (unit, set, 32-head block, head): slots = max_units * G * hblocks * 32.
   // part_out holds each slot block's 32 x d_v values in MFMA-fragment order (see decode.hip),
   // bf16 when the output is bf16, else f32.
@@ -64,6 +65,8 @@ struct PlanArgs {
   int32_t* seqs;
   int32_t* tasks;
   int32_t* multi;
+  int32_t* ccount;        // int32[ccount_n]: combine arrival counters, zeroed by the planner
+  int32_t ccount_n;
   int32_t max_tasks;
   int32_t max_multi;
   int32_t batch;
@@ -95,6 +98,7 @@ struct DecodeArgs {
   const int32_t* multi;
   float* l2_out;
   float* l2_lse;
+  int32_t* ccount;             // [max_tasks][xblocks]: chunk tasks of a sequence that have finished
   int32_t max_tasks, max_multi, xblocks;
   int32_t batch, heads, groups, heads_per_set, rows, max_pages, num_pages, page_size;
   int32_t nsets, hblocks;       // sets per work group, 32-head blocks per set

@@ -42,6 +42,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     const int c = plan_auto_chunk(a, tid);
     if (tid == 0) s_chunk = c;
   }
+  for (int i = tid; i < a.ccount_n; i += blockDim.x) a.ccount[i] = 0;
   __syncthreads();
   const int chunk = s_chunk;
 
@@ -132,8 +133,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
 // A combine task is (sequence, chunk of at most kCombineChunk splits).  Work group (x, t) takes
 // task t and 256 piece positions: one 64-lane piece group per wave, one 1 KB load per split, all
 // of a chunk's loads issued together.  A sequence merged in one chunk is finished there; the
-// chunk results of longer ones (f32, same piece order, with their lse) are merged in chunk order
-// by combine_chunks_kernel, launched after it.
+// chunk results of longer ones are merged in chunk order by the last of their tasks to finish.
 constexpr int kCombineThreads = 256;
 
 struct PieceGroup {
@@ -331,13 +331,44 @@ __global__ __launch_bounds__(kCombineThreads) void combine_ws_kernel(DecodeArgs 
     write_tile(a, d_v, p, b, m.o, lse, tile);
     return;
   }
-  // a chunk of a longer sequence: its merged result, for combine_chunks_kernel
+  // a chunk of a longer sequence: its merged result (f32, same piece order, with its lse)
   const float lse = m.finish();
   const size_t lo = (size_t)(ftask + c) * p.pieces + (size_t)pg * 64 + p.lane;
   float4* dst = reinterpret_cast<float4*>(a.l2_out + lo * vals);
   dst[0] = make_float4(m.o[0], m.o[1], m.o[2], m.o[3]);
   if (vals == 8) dst[1] = make_float4(m.o[4], m.o[5], m.o[6], m.o[7]);
   a.l2_lse[lo] = lse;
+  // The last of the sequence's nc chunk tasks to finish (for this work group's piece positions)
+  // merges the chunk results in chunk order.  Release: every wave's results are stored and fenced
+  // before the arrival is counted; acquire: the last arriver fences before reading the others'.
+  // It resets the counter for the next call (the planner zeroes it too).
+  __shared__ int s_last;
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int* ctr = a.ccount + (size_t)ftask * a.xblocks + blockIdx.x;
+    s_last = atomicAdd(ctr, 1) == nc - 1;
+    if (s_last) *ctr = 0;
+  }
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();
+  Merge mm;
+  for (int q0 = 0; q0 < nc; q0 += kBatch) {
+    float ls[kBatch], v[kBatch][8];
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      const size_t l2 = (size_t)(ftask + min(q0 + k, nc - 1)) * p.pieces + (size_t)pg * 64 + p.lane;
+      ls[k] = a.l2_lse[l2];
+      const float4* src = reinterpret_cast<const float4*>(a.l2_out + l2 * vals);
+      const float4 x0 = src[0];
+      const float4 x1 = vals == 8 ? src[1] : make_float4(0.f, 0.f, 0.f, 0.f);
+      v[k][0] = x0.x, v[k][1] = x0.y, v[k][2] = x0.z, v[k][3] = x0.w;
+      v[k][4] = x1.x, v[k][5] = x1.y, v[k][6] = x1.z, v[k][7] = x1.w;
+    }
+    mm.add(ls, v, nc - q0, vals);
+  }
+  write_piece(a, d_v, p, b, mm.o, mm.finish());
 }
 
 // Batches of a few long sequences (many splits each): work group (x, b) merges piece group x of
@@ -437,36 +468,6 @@ __global__ __launch_bounds__(kSeqWaves * 64) void combine_seq_kernel(DecodeArgs 
   write_piece(a, d_v, p, b, m.o, lse);
 }
 
-// Merge the chunk results of the sequences combined in more than one chunk, in chunk order.  The
-// grid's second dimension strides over those sequences.
-__global__ __launch_bounds__(kCombineThreads) void combine_chunks_kernel(DecodeArgs a, int d_v) {
-  const int pg = 4 * blockIdx.x + (threadIdx.x >> 6);
-  const PieceGroup p = piece_group(a, d_v, pg);
-  const int vals = a.part_bf16 ? 8 : 4;
-  for (int i = blockIdx.y; i < a.header[3]; i += gridDim.y) {
-    const int b = a.multi[i];
-    const int ftask = a.seqs[4 * b + 2];
-    const int nc = a.seqs[4 * b + 3];
-    Merge m;
-    for (int q0 = 0; q0 < nc; q0 += kBatch) {
-      float ls[kBatch], v[kBatch][8];
-#pragma unroll
-      for (int k = 0; k < kBatch; ++k) {
-        const size_t lo = (size_t)(ftask + min(q0 + k, nc - 1)) * p.pieces + (size_t)pg * 64 + p.lane;
-        ls[k] = a.l2_lse[lo];
-        const float4* src = reinterpret_cast<const float4*>(a.l2_out + lo * vals);
-        const float4 x0 = src[0];
-        const float4 x1 = vals == 8 ? src[1] : make_float4(0.f, 0.f, 0.f, 0.f);
-        v[k][0] = x0.x, v[k][1] = x0.y, v[k][2] = x0.z, v[k][3] = x0.w;
-        v[k][4] = x1.x, v[k][5] = x1.y, v[k][6] = x1.z, v[k][7] = x1.w;
-      }
-      m.add(ls, v, nc - q0, vals);
-    }
-    const float lse = m.finish();
-    write_piece(a, d_v, p, b, m.o, lse);
-  }
-}
-
 __global__ __launch_bounds__(kCombineThreads) void combine_rows_kernel(int num_rows, int d_v, int max_splits,
                                                                        const float* part_out, const float* part_lse,
                                                                        const int32_t* nsplits, int out_bf16,
@@ -525,11 +526,6 @@ int launch_combine_ws(const DecodeArgs& a, int32_t d_v, void* stream) {
     return (int)hipGetLastError();
   }
   hipLaunchKernelGGL(combine_ws_kernel, dim3(a.xblocks, a.max_tasks), dim3(kCombineThreads), 0,
-                     static_cast<hipStream_t>(stream), a, d_v);
-  int r = (int)hipGetLastError();
-  if (r != 0 || a.max_multi == 0) return r;
-  const int ys = a.max_multi < 2 ? a.max_multi : 2;  // sequences strided over by the grid
-  hipLaunchKernelGGL(combine_chunks_kernel, dim3(a.xblocks, ys), dim3(kCombineThreads), 0,
                      static_cast<hipStream_t>(stream), a, d_v);
   return (int)hipGetLastError();
 }

@@ -160,6 +160,14 @@ def test_mla_bf16_one_long_sequence_many_splits():
     _check(inp)
 
 
+# a batch above the one-launch combine limit in which one sequence is merged in several chunks
+# (its last chunk task to finish merges the chunk results)
+def test_mla_bf16_multi_chunk_sequence_in_a_large_batch():
+    lens = [40000] + [300 + 97 * i for i in range(9)]
+    inp = synth.make_inputs("mla", len(lens), 128, 1, 512, 64, lens, scale=1 / math.sqrt(192), seed=24)
+    _check(inp)
+
+
 @pytest.mark.parametrize("splits", [9, 40])
 def test_mla_bf16_forced_many_splits(splits):
     inp = synth.make_inputs("mla", 3, 128, 1, 512, 64, [5000, 64, 2600], scale=1 / math.sqrt(192), seed=23)
