@@ -119,6 +119,16 @@ def _kernel_rows(trace_dir: str):
         return list(csv.DictReader(f))
 
 
+def _last_calls_us(trace_dir: str, n: int):
+    """Average duration (us) of each kernel's last n dispatches (the timed part of the run)."""
+    with open(os.path.join(trace_dir, "run_kernel_trace.csv")) as f:
+        rows = sorted(csv.DictReader(f), key=lambda r: int(r["Start_Timestamp"]))
+    per = {}
+    for r in rows:
+        per.setdefault(r["Kernel_Name"], []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    return {k: sum(v[-n:]) / len(v[-n:]) for k, v in per.items()}
+
+
 def _counter(dir_: str, name: str):
     rows = list(csv.DictReader(open(os.path.join(dir_, "run_counter_collection.csv"))))
     out = {}
@@ -153,12 +163,16 @@ def summarize_profile(workload: str, trace_dir: str, fetch_dir: str, write_dir: 
     with open(traffic_path(workload), "w") as f:
         json.dump(t, f, indent=1)
         f.write("\n")
+    last = _last_calls_us(trace_dir, 40)
     lines = [f"# decode_kernel, workload {workload}", "",
-             "Kernel durations (rocprofv3 kernel trace, whole run incl. warm-up):", "",
+             "Kernel durations (rocprofv3 kernel trace; the average over the whole run includes the warm-up,",
+             "whose first launches run at lower clocks; the last 40 calls are the timed part of the run):", "",
              f"    {commands[0]}", "",
-             "| kernel | calls | average us | min us | max us |", "|---|---|---|---|---|"]
+             "| kernel | calls | average us | last 40 calls, average us | min us | max us |",
+             "|---|---|---|---|---|---|"]
     for r in stats:
         lines.append(f"| {r['Name'][:90]} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                     f"{last.get(r['Name'], float('nan')):.1f} | "
                      f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} |")
     lines += ["", "HBM traffic of one decode launch (TCC counters, one pass per counter):", ""]
     lines += [f"    {c}" for c in commands[1:]]
@@ -179,6 +193,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="mla_b64_l4k")
     ap.add_argument("--copies", type=int, default=4, help="cache copies rotated across steps")
+    ap.add_argument("--min-warmup-ms", type=float, default=50.0,
+                    help="keep running untimed warmup steps until this much wall time has passed")
     ap.add_argument("--num-splits", type=int, default=0)
     ap.add_argument("--graph", action="store_true",
                     help="time each step as the replay of a HIP graph holding its plan, decode and combine launches "
@@ -235,9 +251,20 @@ def main() -> int:
     gen_s = time.perf_counter() - t_gen
 
     stream = torch.cuda.current_stream(dev)
+    # W warmup steps, continued (untimed) until the GPU has run steps for at least --min-warmup-ms:
+    # its clocks take tens of milliseconds of load to settle (a step timed after 10 warmup steps
+    # of ~0.12 ms each runs ~20% slower than after 200)
+    t_wu = time.perf_counter()
+    warmup_run = 0
     for i in range(args.warmup):
         decs[i % len(decs)].run()
+        warmup_run += 1
     torch.cuda.synchronize()
+    while (time.perf_counter() - t_wu) * 1e3 < args.min_warmup_ms:
+        for i in range(10):
+            decs[(warmup_run + i) % len(decs)].run()
+        warmup_run += 10
+        torch.cuda.synchronize()
 
     # ---- the timed steps: plan + decode + combine, K times back to back, launched eagerly; with
     # --graph each step is instead the replay of a HIP graph holding the step's launches (one graph per
@@ -362,6 +389,7 @@ def main() -> int:
         "n_gpus": 1,
         "steps": K,
         "warmup": args.warmup,
+        "warmup_steps_run": warmup_run,
         "ms_per_step": round(ms, 5),
         "higher_is_better": True,
         "scaling": "weak",
