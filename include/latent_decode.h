@@ -148,7 +148,10 @@ int32_t ld_workspace_size(const ld_problem* p, size_t* bytes);
 
 /* One decode step: plan the split-KV work list from seq_lens, run the decode
  * kernel over every (sequence, token chunk), and merge the chunks of split
- * sequences with the log-sum-exp rule.  Asynchronous on `stream`.
+ * sequences with the log-sum-exp rule.  Asynchronous on `stream`; two launches:
+ * the decode kernel derives the plan itself (the planner rule of ld_plan) and
+ * leaves the plan in the workspace, then the combine.  The results are the
+ * same bits as ld_plan + ld_decode_planned + ld_combine_planned.
  * workspace: device buffer of at least ld_workspace_size bytes, 256-byte
  * aligned, owned by the caller and not used concurrently by another call. */
 int32_t ld_latent_decode(const ld_problem* p, const void* q_latent, const void* q_rope,
