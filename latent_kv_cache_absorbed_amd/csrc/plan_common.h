@@ -35,10 +35,17 @@ __device__ __forceinline__ int plan_auto_chunk(const PlanArgs& a, int lane) {
   unsigned pg[kCachedLens];
   unsigned mx = 0, sum = 0;
   const int kk = min(kCachedLens, (a.batch + 63) / 64);  // cached rows in use (uniform)
+  // every load is issued before any is used (indices past the batch read sequence 0 and are masked)
+  int raw[kCachedLens];
 #pragma unroll
   for (int k = 0; k < kCachedLens; ++k) {
     const int b = lane + 64 * k;
-    pg[k] = (k < kk && b < a.batch) ? pages_of(b) : 0u;
+    raw[k] = a.seq_lens[b < a.batch ? b : 0];
+  }
+#pragma unroll
+  for (int k = 0; k < kCachedLens; ++k) {
+    const int b = lane + 64 * k;
+    pg[k] = (k < kk && b < a.batch) ? (unsigned)((plan_clampi(raw[k], 0, a.capacity) + page - 1) / page) : 0u;
     mx = max(mx, pg[k]);
     sum = min(sum + pg[k], 1u << 30);
   }
