@@ -37,7 +37,7 @@ METRIC = "decode-attn KV GB/s + tokens/s vs 1-GPU HBM/MFMA roofline, MLA 128h@4K
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
 MFMA_F32_PEAK_TFLOPS = 157.3
-DECODE_SRC = [os.path.join(ROOT, "latent_kv_cache_absorbed_amd", "csrc", f) for f in ("decode.hip", "decode_common.h")]
+DECODE_SRC = [os.path.join(ROOT, "latent_kv_cache_absorbed_amd", "csrc", f) for f in ("decode.hip", "decode_common.h", "plan_common.h")]
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -51,7 +51,7 @@ def flops_per_token_head(w) -> int:
 
 
 def source_sha() -> str:
-    """Hash of the decode kernel's sources (the kernel file and the device header it includes)."""
+    """Hash of the decode kernel's sources (the kernel file and the device headers it includes)."""
     h = hashlib.sha256()
     for path in DECODE_SRC:
         with open(path, "rb") as f:
