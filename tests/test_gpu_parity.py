@@ -215,6 +215,45 @@ def test_fused_plan_matches_staged_plan(variant, H, G, d, dr, lens, splits, kv):
     assert not torch.isnan(fused.out).any()
 
 
+# --- the device planner (ld_plan's kernel and the decode kernel's fused prologue) against the host
+# planner ld_plan_host: unit count and chunk (header words 0 and 1, at the start of the workspace)
+# and every unit record (from byte 256), for batches within one wave of lengths, above it (the
+# lengths are cached 64 per register) and above the 1,024 cached lengths
+@pytest.mark.parametrize("lens_kind,splits", [("one_long", 0), ("b64", 0), ("b300", 0), ("b1500", 0), ("b300", 3)])
+def test_device_plan_matches_host_plan(lens_kind, splits):
+    import latent_kv_cache_absorbed_amd as lkd
+    from gpu_util import to_dev
+    r = np.random.default_rng(41)
+    lens = {"one_long": [40000], "b64": list(r.integers(1, 5000, 64)),
+            "b300": list(r.integers(0, 700, 300)), "b1500": list(r.integers(0, 300, 1500))}[lens_kind]
+    inp = synth.make_inputs("mla", len(lens), 128, 1, 512, 64, lens, scale=_S, seed=42)
+    print(f"case device plan {lens_kind} splits={splits} B={len(lens)}", flush=True)
+    bt = torch.from_numpy(inp.layout.block_table).cuda()
+    sl = torch.from_numpy(inp.layout.seq_lens).cuda()
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    for fused in (False, True):
+        d = lkd.Decoder(to_dev(inp.q_lat), to_dev(inp.q_rope), to_dev(inp.k_pool), bt, sl, variant="mla",
+                        scale=inp.scale, num_splits=splits)
+        d.workspace.fill_(0xFF)
+        if fused:
+            d.run()
+        else:
+            d.plan()
+        torch.cuda.synchronize()
+        chunk, units, ns, first = lkd.plan_host(d.problem, inp.layout.seq_lens, cus)
+        ws = d.workspace.cpu().numpy()
+        header = ws[:16].view(np.int32)
+        assert header[0] == units and (splits > 0 or header[1] == chunk), (header[:2], units, chunk)
+        rec = ws[256:256 + 16 * units].view(np.int32).reshape(units, 4)
+        for b in range(len(lens)):
+            if ns[b] == 0:
+                continue
+            ck = chunk if splits == 0 else max(64, -(-(-(-int(lens[b]) // splits)) // 64) * 64)
+            for s_ in range(ns[b]):
+                u = first[b] + s_
+                assert list(rec[u]) == [b, s_ * ck, min(int(lens[b]), (s_ + 1) * ck), s_], (fused, b, s_, rec[u])
+
+
 # --- the whole step (plan + decode + one- and two-level combine) captured in a HIP graph: every
 # replay, with eager work on the same buffers in between, reproduces the eager result bit for bit
 @pytest.mark.parametrize("lens", [[1500, 77, 3000], [40000]])
