@@ -84,12 +84,22 @@ int32_t rows_per_seq(const ld_problem& p) {
   return p.variant == LD_VARIANT_MLRA ? p.num_q_heads * p.num_groups : p.num_q_heads;
 }
 
-// Units the automatic planner aims for: one wave of work groups over the chip.
-int32_t target_units_for(const ld_problem& p, int32_t num_cus) {
+// Units the automatic planner aims for: one wave of work groups over the chip, i.e. as many work
+// groups per CU as can be resident at once (at most 4; several for the small work groups of the
+// shared-KV and one-share shapes, one for the 8-wave latent shapes).  The finer split applies only
+// while units keep kMinChunkPages pages (see plan_common.h).
+int32_t base_units_for(const ld_problem& p, int32_t num_cus) {
   const Shape s = launch_shape(p);
   const int wpu = s.wg_per_unit > 0 ? s.wg_per_unit : 1;
-  int t = num_cus / wpu;
+  const int t = num_cus / wpu;
   return t < 1 ? 1 : t;
+}
+
+int32_t target_units_for(const ld_problem& p, int32_t num_cus) {
+  const Shape s = launch_shape(p);
+  int occ = s.nsets > 0 ? decode_wgs_per_cu(p, s.nsets, s.hblocks) : 1;
+  occ = occ < 1 ? 1 : (occ > 4 ? 4 : occ);
+  return base_units_for(p, num_cus) * occ;
 }
 
 // A unit spans at most kUnitPages pages, so a sequence has at most ceil(max_pages / kUnitPages)
@@ -196,20 +206,26 @@ int32_t ld_plan_host(const ld_problem* p, const int32_t* seq_lens_host, int32_t 
   long long chunk = 0;
   if (p->num_splits == 0) {
     // the smallest multiple of the page that gives at most `target` units (bisection on pages)
-    const long long target = target_units_for(*p, num_cus);
     long long mx = 0;
     for (int b = 0; b < p->batch; ++b) mx = std::max(mx, clampL(seq_lens_host[b]));
-    long long lo = 1, hi = std::max(1LL, (mx + page - 1) / page);
-    while (lo < hi) {
-      const long long mid = (lo + hi) / 2, c = mid * page;
-      long long cnt = 0;
-      for (int b = 0; b < p->batch; ++b) cnt += (clampL(seq_lens_host[b]) + c - 1) / c;
-      if (cnt <= target)
-        hi = mid;
-      else
-        lo = mid + 1;
-    }
-    chunk = std::min(lo, (long long)kUnitPages) * page;
+    auto chunk_for = [&](long long target) {
+      long long lo = 1, hi = std::max(1LL, (mx + page - 1) / page);
+      while (lo < hi) {
+        const long long mid = (lo + hi) / 2, c = mid * page;
+        long long cnt = 0;
+        for (int b = 0; b < p->batch; ++b) cnt += (clampL(seq_lens_host[b]) + c - 1) / c;
+        if (cnt <= target)
+          hi = mid;
+        else
+          lo = mid + 1;
+      }
+      return std::min(lo, (long long)kUnitPages) * page;
+    };
+    // the finer target (several resident work groups per CU) down to kMinChunkPages pages, never
+    // coarser than one unit per CU
+    const long long base = base_units_for(*p, num_cus), target = target_units_for(*p, num_cus);
+    const long long c1 = chunk_for(base);
+    chunk = target == base ? c1 : std::max(chunk_for(target), std::min(c1, (long long)kMinChunkPages * page));
   }
   long long units = 0;
   for (int b = 0; b < p->batch; ++b) {
@@ -330,6 +346,7 @@ PlanArgs plan_args(const ld_problem* p, const WsLayout& w, void* workspace, cons
   pa.capacity = p->max_pages_per_seq * p->page_size;
   pa.page_size = p->page_size;
   pa.target_units = target_units_for(*p, device_cu_count());
+  pa.base_units = base_units_for(*p, device_cu_count());
   pa.forced_splits = p->num_splits;
   pa.max_units = w.max_units;
   return pa;

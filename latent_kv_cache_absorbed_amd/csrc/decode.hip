@@ -821,6 +821,30 @@ int launch_decode(const ld_problem& p, const DecodeArgs& a, void* stream) {
   return -1;
 }
 
+// Work groups of a shape's decode kernel that can be resident on one CU at once (registers, LDS,
+// waves), as the runtime reports it; 1 when it cannot be queried (no device).  Cached per shape.
+template <int KV, int DL, int DR, int KIND, int NSETS, int HB, int SPLIT>
+int wgs_per_cu_of() {
+  static const int n = [] {
+    int v = 0;
+    const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+        &v, reinterpret_cast<const void*>(decode_kernel<KV, DL, DR, KIND, NSETS, HB, SPLIT>), NSETS * HB * SPLIT * kWaveSize,
+        0);
+    return (e == hipSuccess && v > 0) ? v : 1;
+  }();
+  return n;
+}
+
+int decode_wgs_per_cu(const ld_problem& p, int nsets, int hblocks) {
+  const int kv = kv_code(p), kind = kind_code(p), dl = p.d_latent, dr = p.d_rope;
+#define LD_OCC(KV_, DL_, DR_, KIND_, NS_, HB_, SP_) \
+  if (kv == KV_ && dl == DL_ && dr == DR_ && kind == KIND_ && nsets == NS_ && hblocks == HB_) \
+    return wgs_per_cu_of<KV_, DL_, DR_, KIND_, NS_, HB_, SP_>();
+  LD_SHAPES(LD_OCC)
+#undef LD_OCC
+  return 1;
+}
+
 int device_cu_count() {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 256;

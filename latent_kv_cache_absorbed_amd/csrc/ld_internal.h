@@ -21,6 +21,9 @@ constexpr int kWaveSize = 64;
 constexpr int kPlanThreads = 256;
 constexpr int kCombineChunk = 16;     // splits merged by one combine task
 constexpr int kUnitPages = 512;       // pages a work unit spans at most (its block-table entries fit in LDS)
+// The planner splits finer than one unit per CU (to fill several resident work groups per CU) only
+// while units keep at least this many pages.
+constexpr int kMinChunkPages = 16;
 // Batches of at most this many sequences are combined by one launch of wide work groups (each
 // sequence then has many splits); larger batches by per-task work groups and a chunk merge.
 constexpr int kSeqCombineMaxBatch = 8;
@@ -72,7 +75,8 @@ struct PlanArgs {
   int32_t batch;
   int32_t capacity;       // max_pages_per_seq * page_size
   int32_t page_size;
-  int32_t target_units;   // units the planner aims for (auto mode)
+  int32_t target_units;   // units the planner aims for (auto mode): resident work groups over the chip
+  int32_t base_units;     // one work group per CU; the finer target applies down to kMinChunkPages
   int32_t forced_splits;  // 0 = auto
   int32_t max_units;
 };
@@ -119,6 +123,7 @@ struct DecodeArgs {
 // Host planner rule shared (as a specification, not as code) with the device
 // planner: see plan_chunk() in api.cpp and plan_kernel in plan_combine.hip.
 int32_t target_units_for(const ld_problem& p, int32_t num_cus);
+int32_t base_units_for(const ld_problem& p, int32_t num_cus);
 int32_t max_units_for(const ld_problem& p, int32_t num_cus);
 int32_t rows_per_seq(const ld_problem& p);
 
@@ -157,6 +162,7 @@ int launch_head_projection(const ProjArgs& a, int out_bf16, void* stream);
 // Whether a decode kernel is built for p's dtype/dims/kind with `nsets` sets per work group and
 // `hblocks` 32-head blocks per set.
 bool decode_instantiated(const ld_problem& p, int nsets, int hblocks);
+int decode_wgs_per_cu(const ld_problem& p, int nsets, int hblocks);
 int device_cu_count();
 
 }  // namespace ld

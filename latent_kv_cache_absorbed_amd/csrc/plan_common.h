@@ -2,8 +2,10 @@
 // fused-plan prologue (the host computes the same rule in plan_host, api.cpp).
 //
 //   L_b   = clamp(seq_lens[b], 0, capacity)
-//   auto:   chunk = the smallest multiple of page with sum_b ceil(L_b / chunk) <= target_units
-//           (roundup(max_b L_b, page) when none is);                          n_b = ceil(L_b / chunk)
+//   auto:   chunk(T) = the smallest multiple of page with sum_b ceil(L_b / chunk) <= T
+//           (roundup(max_b L_b, page) when none is); with T1 = one work group per CU (base_units)
+//           and T2 = the resident work groups over the chip (target_units, a multiple of T1),
+//           chunk = max(chunk(T2), min(chunk(T1), kMinChunkPages * page));    n_b = ceil(L_b / chunk)
 //   forced: chunk_b = max(page, roundup(ceil(L_b / splits), page));        n_b = ceil(L_b / chunk_b)
 //   either chunk is capped at kUnitPages pages
 //   units of sequence b are first_b .. first_b + n_b - 1 (first_b = exclusive prefix sum of n_b),
@@ -69,21 +71,26 @@ __device__ __forceinline__ int plan_auto_chunk(const PlanArgs& a, int lane) {
   };
   // sum_b ceil(P_b / k) >= sum_b P_b / k, so no k below ceil(sum / target) qualifies; for
   // balanced lengths that bound usually does
-  const unsigned tu = (unsigned)a.target_units;
-  unsigned lo = max(1u, (sum + tu - 1) / tu), hi = max(mx, 1u);
-  if (lo >= hi || count(lo) <= tu) {
-    hi = lo = min(lo, hi);
-  } else {
-    lo = lo + 1;
-  }
-  while (lo < hi) {  // uniform across the wave
-    const unsigned mid = (lo + hi) >> 1;
-    if (count(mid) <= tu)
-      hi = mid;
-    else
-      lo = mid + 1;
-  }
-  return (int)min(lo, (unsigned)kUnitPages) * page;
+  auto chunk_pages = [&](unsigned tu) {
+    unsigned lo = max(1u, (sum + tu - 1) / tu), hi = max(mx, 1u);
+    if (lo >= hi || count(lo) <= tu) {
+      hi = lo = min(lo, hi);
+    } else {
+      lo = lo + 1;
+    }
+    while (lo < hi) {  // uniform across the wave
+      const unsigned mid = (lo + hi) >> 1;
+      if (count(mid) <= tu)
+        hi = mid;
+      else
+        lo = mid + 1;
+    }
+    return min(lo, (unsigned)kUnitPages);
+  };
+  const unsigned c1 = chunk_pages((unsigned)a.base_units);
+  if (a.target_units == a.base_units) return (int)c1 * page;
+  const unsigned c2 = chunk_pages((unsigned)a.target_units);
+  return (int)max(c2, min(c1, (unsigned)kMinChunkPages)) * page;
 }
 
 // One sequence's share of the plan: clamped length, chunk, units, combine tasks, multi flag.
