@@ -85,6 +85,22 @@ def test_gla2_one_group(kv):
     _check(inp)
 
 
+# fp8 caches over the other kernel shapes, with units of none, one, two and many stages and forced
+# splits: MLRA-4 (two branches per work group), one 256-dim latent shared by 128 heads (four head
+# blocks), GLA-4 (four groups per work group) and MLA
+@pytest.mark.parametrize("variant,G,d,lens", [
+    ("mlra", 4, 128, [1, 32, 33, 64, 65, 3000]),
+    ("gla", 1, 256, [1, 31, 96, 2049]),
+    ("gla", 4, 256, [2, 160, 1025]),
+    ("mla", 1, 512, [0, 33, 130, 3001]),
+])
+def test_fp8_shapes(variant, G, d, lens):
+    inp = synth.make_inputs(variant, len(lens), 128, G, d, 64, lens, scale=1 / math.sqrt(192), seed=23,
+                            kv_dtype="fp8_e4m3")
+    _check(inp)
+    _check(inp, num_splits=5)
+
+
 def test_mla_fp8():
     inp = synth.make_inputs("mla", 2, 128, 1, 512, 64, [600, 65], scale=1 / math.sqrt(192), seed=15,
                             kv_dtype="fp8_e4m3")
