@@ -26,6 +26,9 @@ def _gpu():
     ("gla2_fp8_b64_mixed", [0, 17, 63], [0, 63, 64, 127]),
     ("mqa_b32_l32k", [0, 31], [0, 63]),
     ("gta_b32_l32k", [5], [0, 9, 63]),
+    ("mla_b1_l1m", [0], [0, 127]),
+    ("mlra4_tp4_share_b1_l1m", [0], [0, 101]),
+    ("gla2_tp2_share_fp8_b64_mixed", [1, 40], [0, 33, 63]),
 ])
 def test_full_size_sampled(name, batches, heads):
     inp = synth.make_workload_inputs(synth.WORKLOADS[name])
