@@ -142,8 +142,10 @@ const char* ld_status_string(int32_t status);
 int32_t ld_check_problem(const ld_problem* p);
 
 /* Bytes of device workspace ld_latent_decode needs for this problem (split-KV
- * partial outputs and the work list).  Depends on the shape only, never on the
- * contents of seq_lens.  Returns LD_OK and writes *bytes, or a shape error. */
+ * partial outputs and the work list).  Depends on the shape and on the current
+ * device (its compute-unit count and how many decode work groups fit on one),
+ * never on the contents of seq_lens: query it with the device current that
+ * will run the calls.  Returns LD_OK and writes *bytes, or a shape error. */
 int32_t ld_workspace_size(const ld_problem* p, size_t* bytes);
 
 /* One decode step: plan the split-KV work list from seq_lens, run the decode
