@@ -286,9 +286,11 @@ __device__ __forceinline__ void write_tile(const DecodeArgs& a, int d_v, const P
 __global__ __launch_bounds__(kCombineThreads) void combine_ws_kernel(DecodeArgs a, int d_v) {
   __shared__ float tile[32 * 65];
   const int t = blockIdx.y;
-  if (t >= a.header[2]) return;
+  // the task record (in bounds for every t < max_tasks) is read together with the task count
+  const int ntask = a.header[2];
   const int b = a.tasks[2 * t];
   const int c = a.tasks[2 * t + 1];
+  if ((t >= ntask) | (b < 0)) return;  // (b >= 0 in every task; testing it keeps both loads before the branch)
   const int first = a.seqs[4 * b + 1];
   const int n = max(0, min(a.seqs[4 * b], a.max_units - first));
   const int ftask = a.seqs[4 * b + 2];
