@@ -789,6 +789,9 @@ int run(const DecodeArgs& a, void* stream) {
   /* GQA: 4 kv heads (K and V) per work group; GTA: 8; MQA: one kv head of 64 or 32 heads */  \
   X(KV_BF16, 128, 0, KIND_SHARED, 4, 1, 1) X(KV_BF16, 128, 0, KIND_SHARED, 2, 1, 1)            \
   X(KV_BF16, 128, 0, KIND_SHARED, 1, 2, 1) X(KV_BF16, 128, 0, KIND_SHARED, 1, 1, 1)            \
+  /* MQA with large head dims (MFA-style single kv head): 256 and 512 */                      \
+  X(KV_BF16, 256, 0, KIND_SHARED, 1, 2, 1) X(KV_BF16, 256, 0, KIND_SHARED, 1, 1, 1)            \
+  X(KV_BF16, 512, 0, KIND_SHARED, 1, 2, 2) X(KV_BF16, 512, 0, KIND_SHARED, 1, 1, 2)            \
   X(KV_BF16, 128, 0, KIND_TIED, 8, 1, 1) X(KV_BF16, 128, 0, KIND_TIED, 4, 1, 1)                \
   X(KV_BF16, 128, 0, KIND_TIED, 1, 2, 1) X(KV_BF16, 128, 0, KIND_TIED, 1, 1, 1)                \
   X(KV_F32, 64, 0, KIND_SHARED, 4, 1, 1) X(KV_F32, 64, 0, KIND_SHARED, 1, 1, 1)                \

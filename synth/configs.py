@@ -82,6 +82,9 @@ WORKLOADS = {
     "gqa_b32_l32k": Workload("gqa_b32_l32k", "gqa", 32, 64, 8, 128, 0, 32768, scale=_S128, seed=4),
     "mqa_b32_l32k": Workload("mqa_b32_l32k", "mqa", 32, 64, 1, 128, 0, 32768, scale=_S128, seed=4),
     "gta_b32_l32k": Workload("gta_b32_l32k", "gta", 32, 64, 8, 128, 0, 32768, scale=_S128, seed=4),
+    # one kv head of a large head dim (the MFA-style cache: MQA with d >> 128)
+    "mqa_d512_b32_l32k": Workload("mqa_d512_b32_l32k", "mqa", 32, 64, 1, 512, 0, 32768,
+                                  scale=1.0 / math.sqrt(512.0), seed=4),
     # GLA-2 over an fp8 latent cache with imbalanced lengths
     "gla2_fp8_b64_mixed": Workload("gla2_fp8_b64_mixed", "gla", 64, 128, 2, 256, 64, ("uniform", 1024, 65536),
                                    kv_dtype="fp8_e4m3", scale=_S192, seed=5),

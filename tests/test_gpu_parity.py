@@ -119,6 +119,20 @@ def test_shared_kv(variant, groups):
     _check(inp)
 
 
+# a single kv head of large head dim (MFA-style MQA) and GQA over 256-dim heads
+@pytest.mark.parametrize("variant,H,G,d,lens", [
+    ("mqa", 64, 1, 256, [5, 300, 1025]),
+    ("mqa", 32, 1, 256, [64, 777]),
+    ("mqa", 64, 1, 512, [1, 130, 2049]),
+    ("mqa", 32, 1, 512, [33, 900]),
+    ("gqa", 32, 4, 256, [250, 3000]),
+])
+def test_shared_kv_large_head_dim(variant, H, G, d, lens):
+    inp = synth.make_inputs(variant, len(lens), H, G, d, 0, lens, scale=1 / math.sqrt(d), seed=24)
+    _check(inp)
+    _check(inp, num_splits=3)
+
+
 def test_shared_kv_f32():
     inp = synth.make_inputs("gqa", 2, 16, 4, 64, 0, [90, 200], scale=0.125, seed=18, kv_dtype="f32", q_dtype="f32",
                             out_dtype="f32")
