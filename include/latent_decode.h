@@ -30,6 +30,11 @@
  *   GTA   GQA whose V is the same tied state as K (GTA/GLA article, section on
  *         Grouped-Tied Attention).
  *
+ * Several query tokens (q_len = Q > 1, MLA and MQA): every query row r becomes Q
+ * rows (i, r), i = 0 .. Q-1, token i seeing the first L_b - Q + 1 + i cache rows
+ * (none when that is not positive: out = 0, lse = -inf); the layouts below then
+ * have Q*H rows per sequence where they have H, row i*H + h.
+ *
  * Layouts (row-major, innermost dimension last):
  *   q_latent  MLA/GLA [B, H, d_latent]; MLRA [B, H, G, d_latent]; GQA/MQA/GTA [B, H, d_latent]
  *   q_rope    MLA/GLA [B, H, d_rope];   MLRA [B, H, G, d_rope];   NULL for GQA/MQA/GTA
@@ -75,7 +80,7 @@
 extern "C" {
 #endif
 
-#define LD_ABI_VERSION 1
+#define LD_ABI_VERSION 2
 
 typedef enum ld_status {
   LD_OK = 0,
@@ -121,6 +126,9 @@ typedef struct ld_problem {
                                 lse is reported in this scaled domain */
   int32_t num_splits;        /* 0: the planner splits long sequences over CUs; n >= 1: at most n splits,
                                 except that no split spans more than 512 pages */
+  int32_t q_len;             /* Q >= 1 query tokens per sequence (several for speculative / multi-token
+                                decode; MLA and MQA only, Q <= 16): query token i sits at position
+                                L_b - Q + i and attends the cache rows 0 .. L_b - Q + i (causal) */
 } ld_problem;
 
 /* Device pointers of the paged cache (see the layouts above). */

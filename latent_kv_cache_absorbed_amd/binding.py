@@ -43,7 +43,8 @@ class Problem(ctypes.Structure):
                 ("num_q_heads", ctypes.c_int32), ("num_groups", ctypes.c_int32), ("d_latent", ctypes.c_int32),
                 ("d_rope", ctypes.c_int32), ("page_size", ctypes.c_int32), ("num_pages", ctypes.c_int32),
                 ("max_pages_per_seq", ctypes.c_int32), ("q_dtype", ctypes.c_int32), ("kv_dtype", ctypes.c_int32),
-                ("out_dtype", ctypes.c_int32), ("softmax_scale", ctypes.c_float), ("num_splits", ctypes.c_int32)]
+                ("out_dtype", ctypes.c_int32), ("softmax_scale", ctypes.c_float), ("num_splits", ctypes.c_int32),
+                ("q_len", ctypes.c_int32)]
 
 
 class KVCache(ctypes.Structure):
@@ -110,10 +111,10 @@ def status_string(status: int) -> str:
 
 def make_problem(variant: str, batch: int, heads: int, groups: int, d_latent: int, d_rope: int, page_size: int,
                  num_pages: int, max_pages_per_seq: int, q_dtype: str, kv_dtype: str, out_dtype: str, scale: float,
-                 num_splits: int = 0) -> Problem:
+                 num_splits: int = 0, q_len: int = 1) -> Problem:
     return Problem(ctypes.sizeof(Problem), VARIANTS[variant], batch, heads, groups, d_latent, d_rope, page_size,
                    num_pages, max_pages_per_seq, DTYPES[q_dtype], DTYPES[kv_dtype], DTYPES[out_dtype], float(scale),
-                   num_splits)
+                   num_splits, q_len)
 
 
 def check_problem(p: Problem) -> int:
@@ -151,12 +152,13 @@ class Decoder:
     (same stream, same workspace), e.g. to plan once for several layers.
     Layouts as in include/latent_decode.h; ``k`` holds the cache rows (for an
     fp8 latent cache: the E4M3 codes as uint8 or float8_e4m3fn, with ``rope``
-    and ``kscale`` beside it).
+    and ``kscale`` beside it).  ``q_len`` > 1 (mla, mqa): q_latent / q_rope, out
+    and lse hold q_len*H rows per sequence, row i*H + h for query token i.
     """
 
     def __init__(self, q_latent, q_rope, k, block_table, seq_lens, *, variant: str, scale: float,
                  groups: int | None = None, v=None, rope=None, kscale=None, out=None, lse=None,
-                 out_dtype: str | None = None, num_splits: int = 0, workspace=None):
+                 out_dtype: str | None = None, num_splits: int = 0, q_len: int = 1, workspace=None):
         if variant not in VARIANTS:
             raise ValueError(f"unknown variant {variant!r}")
         _need(q_latent, "q_latent", (torch.float32, torch.bfloat16))
@@ -168,6 +170,10 @@ class Decoder:
         latent = variant in ("mla", "gla", "mlra")
         B, H = q_latent.shape[0], q_latent.shape[1]
         d = q_latent.shape[-1]
+        if q_len > 1:  # q_latent holds Q*H rows per sequence, row i*H + h
+            if H % q_len:
+                raise ValueError(f"q_latent has {H} rows per sequence, not a multiple of q_len={q_len}")
+            H //= q_len
         if latent:
             _need(q_rope, "q_rope", (q_latent.dtype,))
             dr = q_rope.shape[-1]
@@ -190,14 +196,14 @@ class Decoder:
             raise ValueError(f"groups={groups} does not match the tensors ({G})")
         out_dtype = out_dtype or ("f32" if q_dtype == "f32" else "bf16")
         self.problem = make_problem(variant, B, H, G, d, dr, k.shape[1], k.shape[0], block_table.shape[1], q_dtype,
-                                    kv_dtype, out_dtype, scale, num_splits)
-        rows = H * G if variant == "mlra" else H
+                                    kv_dtype, out_dtype, scale, num_splits, q_len)
+        rows = H * G if variant == "mlra" else H * max(q_len, 1)
         odt = torch.float32 if out_dtype == "f32" else torch.bfloat16
         dev = q_latent.device
         if out is None:
-            out = torch.empty((B, H, G, d) if variant == "mlra" else (B, H, d), dtype=odt, device=dev)
+            out = torch.empty((B, H, G, d) if variant == "mlra" else (B, rows, d), dtype=odt, device=dev)
         if lse is None:
-            lse = torch.empty((B, H, G) if variant == "mlra" else (B, H), dtype=torch.float32, device=dev)
+            lse = torch.empty((B, H, G) if variant == "mlra" else (B, rows), dtype=torch.float32, device=dev)
         _need(out, "out", (odt,))
         _need(lse, "lse", (torch.float32,))
         if out.numel() != B * rows * d or lse.numel() != B * rows:
@@ -250,11 +256,11 @@ class Decoder:
 
 def latent_decode(q_latent, q_rope, k, block_table, seq_lens, *, variant: str, scale: float, groups: int | None = None,
                   v=None, rope=None, kscale=None, out=None, lse=None, out_dtype: str | None = None,
-                  num_splits: int = 0, workspace=None, stream=None):
+                  num_splits: int = 0, q_len: int = 1, workspace=None, stream=None):
     """One decode step; returns (out, lse).  See ``Decoder`` for the arguments."""
     d = Decoder(q_latent, q_rope, k, block_table, seq_lens, variant=variant, scale=scale, groups=groups, v=v,
                 rope=rope, kscale=kscale, out=out, lse=lse, out_dtype=out_dtype, num_splits=num_splits,
-                workspace=workspace)
+                q_len=q_len, workspace=workspace)
     return d.run(stream)
 
 

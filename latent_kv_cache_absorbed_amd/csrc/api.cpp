@@ -25,6 +25,16 @@ struct Shape {
 Shape launch_shape(const ld_problem& p) {
   Shape s;
   const int H = p.num_q_heads, G = p.num_groups;
+  if (p.q_len > 1) {
+    // one work group per query token (the tokens take the place of sets): one-set kernels only
+    s.heads_per_set = H;
+    s.hblocks = (H + 31) / 32;
+    if (decode_instantiated(p, 1, s.hblocks)) {
+      s.nsets = 1;
+      s.wg_per_unit = p.q_len;
+    }
+    return s;
+  }
   s.heads_per_set = p.variant == LD_VARIANT_MLRA ? H : H / G;
   s.hblocks = (s.heads_per_set + 31) / 32;
   for (int n = 8; n >= 1; n >>= 1) {
@@ -49,7 +59,7 @@ WsLayout ws_layout(const ld_problem& p, int num_cus) {
   off = round256(off + (size_t)w.max_units * sizeof(Unit));
   w.seqs = off;
   off = round256(off + (size_t)p.batch * 4 * sizeof(int32_t));
-  const size_t slots = (size_t)w.max_units * p.num_groups * launch_shape(p).hblocks * 32;
+  const size_t slots = (size_t)w.max_units * query_sets(p) * launch_shape(p).hblocks * 32;
   w.part_lse = off;
   off = round256(off + slots * sizeof(float));
   w.part_out = off;
@@ -59,7 +69,7 @@ WsLayout ws_layout(const ld_problem& p, int num_cus) {
   w.max_tasks = p.num_splits > 0 ? p.batch * ((p.num_splits + kCombineChunk - 1) / kCombineChunk)
                                  : (w.max_units + kCombineChunk - 1) / kCombineChunk + p.batch;
   const size_t vals = p.out_dtype == LD_BF16 ? 8 : 4;   // values per piece
-  const size_t pieces = (size_t)p.num_groups * launch_shape(p).hblocks * (w.d_v / 32) * (16 / vals) * 64;
+  const size_t pieces = (size_t)query_sets(p) * launch_shape(p).hblocks * (w.d_v / 32) * (16 / vals) * 64;
   w.xblocks = (int32_t)(pieces / 256);
   w.tasks = off;
   off = round256(off + (size_t)w.max_tasks * 2 * sizeof(int32_t));
@@ -81,8 +91,12 @@ WsLayout ws_layout(const ld_problem& p, int num_cus) {
 }  // namespace
 
 int32_t rows_per_seq(const ld_problem& p) {
+  if (p.q_len > 1) return p.q_len * p.num_q_heads;
   return p.variant == LD_VARIANT_MLRA ? p.num_q_heads * p.num_groups : p.num_q_heads;
 }
+
+// Sets of query rows (their partial blocks and combine pieces): groups, or the query tokens
+int32_t query_sets(const ld_problem& p) { return p.q_len > 1 ? p.q_len : p.num_groups; }
 
 // Units the automatic planner aims for: one wave of work groups over the chip, i.e. as many work
 // groups per CU as can be resident at once (at most 4; several for the small work groups of the
@@ -148,6 +162,8 @@ int32_t ld_check_problem(const ld_problem* p) {
     return LD_ERR_BAD_SHAPE;
   if ((long long)p->max_pages_per_seq * p->page_size > 0x7fffffffLL) return LD_ERR_BAD_SHAPE;
   if (p->num_splits < 0) return LD_ERR_BAD_SHAPE;
+  if (p->q_len < 1 || p->q_len > 16) return LD_ERR_BAD_SHAPE;
+  if (p->q_len > 1 && p->variant != LD_VARIANT_MLA && p->variant != LD_VARIANT_MQA) return LD_ERR_UNSUPPORTED;
   if (!std::isfinite(p->softmax_scale) || !(p->softmax_scale > 0.f)) return LD_ERR_BAD_SHAPE;
   const int H = p->num_q_heads, G = p->num_groups;
   switch (p->variant) {
@@ -311,8 +327,10 @@ DecodeArgs decode_args(const ld_problem* p, const WsLayout& w, void* workspace) 
   a.max_multi = w.max_multi;
   a.xblocks = w.xblocks;
   a.batch = p->batch;
-  a.heads = p->num_q_heads;
-  a.groups = p->num_groups;
+  a.heads = p->num_q_heads * (p->q_len > 1 ? p->q_len : 1);
+  a.groups = query_sets(*p);
+  a.qlen = p->q_len;
+  a.cache_groups = p->num_groups;
   a.heads_per_set = s.heads_per_set;
   a.rows = w.rows;
   a.max_pages = p->max_pages_per_seq;

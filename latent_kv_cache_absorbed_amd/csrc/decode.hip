@@ -296,6 +296,13 @@ __global__ __launch_bounds__(NSETS* HB* SPLIT * 64) void decode_kernel(DecodeArg
 
   const int set0 = sb * NSETS;
   const int G = a.groups;
+  // several query tokens per sequence: the work group's set is its token, which sees the first
+  // L_b - qlen + 1 + set0 cache rows; every token reads the cache's one latent / kv head
+  if (a.qlen > 1) {
+    const int Lb = clampi(a.seq_lens[b], 0, a.max_pages * a.page_size);
+    t_end = max(t_begin, min(t_end, Lb - a.qlen + 1 + set0));
+  }
+  const int lset0 = a.qlen > 1 ? 0 : set0;  // first cache set (latent slice / kv head) read
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform, kept in an SGPR
   const int lane = threadIdx.x & 63;
   const int h = lane >> 5;
@@ -320,7 +327,8 @@ __global__ __launch_bounds__(NSETS* HB* SPLIT * 64) void decode_kernel(DecodeArg
 
   // global row geometry (bytes): latent variants store [G latents | rope] per token (fp8: codes
   // only, the rope key lives in its own pool); GQA/MQA/GTA store [G kv heads][DL] per token
-  const int grow_bytes = (KIND == KIND_LATENT) ? (G * DL * C::GES + (KV == KV_FP8 ? 0 : DR * ES)) : G * DL * ES;
+  const int CG = a.cache_groups;
+  const int grow_bytes = (KIND == KIND_LATENT) ? (CG * DL * C::GES + (KV == KV_FP8 ? 0 : DR * ES)) : CG * DL * ES;
   const char* kbase = static_cast<const char*>(a.k);
 
   // ---- issue the copies of one stage into buffer `buf`
@@ -337,7 +345,7 @@ __global__ __launch_bounds__(NSETS* HB* SPLIT * 64) void decode_kernel(DecodeArg
     if constexpr (KV != KV_FP8) {
       dma_region<C::LW, C::MLS, C::DMA_WAVES, 0>(buf + C::LAT_OFF, wave, lane, krows, grow_bytes, tlast, [&](int cb) {
         const int s2 = cb / (DL * ES);
-        return (set0 + s2) * DL * ES + (cb - s2 * DL * ES);
+        return (lset0 + s2) * DL * ES + (cb - s2 * DL * ES);
       });
     } else {
       // codes -> registers now; converted and written after this stage's compute
@@ -350,7 +358,7 @@ __global__ __launch_bounds__(NSETS* HB* SPLIT * 64) void decode_kernel(DecodeArg
           const int s2 = (k16 * 16) / DL;
           const int w = k16 * 16 - s2 * DL;
           pre[r] = *reinterpret_cast<const uint4*>(kbase + (r0 + min(t, tlast)) * (size_t)grow_bytes +
-                                                   (size_t)(set0 + s2) * DL + w);
+                                                   (size_t)(lset0 + s2) * DL + w);
         }
       }
       if (threadIdx.x < kTile) pre_sc = a.kscale[r0 + min((int)threadIdx.x, tlast)];
@@ -362,7 +370,7 @@ __global__ __launch_bounds__(NSETS* HB* SPLIT * 64) void decode_kernel(DecodeArg
                                                   [&](int cb) { return cb; });
       } else {
         dma_region<C::RW, C::MR, C::DMA_WAVES, kTile * C::LW / 1024>(buf + C::ROPE_OFF, wave, lane, krows, grow_bytes,
-                                                                     tlast, [&](int cb) { return G * DL * ES + cb; });
+                                                                     tlast, [&](int cb) { return CG * DL * ES + cb; });
       }
     }
     if constexpr (KIND == KIND_SHARED) {
@@ -370,7 +378,7 @@ __global__ __launch_bounds__(NSETS* HB* SPLIT * 64) void decode_kernel(DecodeArg
       dma_region<C::VW, C::MV, C::DMA_WAVES, kTile *(C::LW + C::RW) / 1024>(
           buf + C::V_OFF, wave, lane, vrows, grow_bytes, tlast, [&](int cb) {
             const int s2 = cb / (DL * ES);
-            return (set0 + s2) * DL * ES + (cb - s2 * DL * ES);
+            return (lset0 + s2) * DL * ES + (cb - s2 * DL * ES);
           });
     }
   };

@@ -111,6 +111,10 @@ struct DecodeArgs {
   int32_t out_bf16;
   int32_t part_bf16;            // partials stored as bf16 (else f32)
   int32_t mlra;
+  // Several query tokens per sequence (qlen > 1, MLA and MQA): the tokens take the place of sets
+  // (groups = qlen, heads = qlen * H); all read the cache's one latent / kv head (cache_groups = 1),
+  // token i seeing the first L_b - qlen + 1 + i rows.
+  int32_t qlen, cache_groups;
   float scale_log2;             // softmax_scale * log2(e)
   // Fused plan (ld_latent_decode): every work group derives its unit from seq_lens with the
   // planner rule instead of reading the plan arrays, and the work groups write those arrays for
@@ -126,6 +130,7 @@ int32_t target_units_for(const ld_problem& p, int32_t num_cus);
 int32_t base_units_for(const ld_problem& p, int32_t num_cus);
 int32_t max_units_for(const ld_problem& p, int32_t num_cus);
 int32_t rows_per_seq(const ld_problem& p);
+int32_t query_sets(const ld_problem& p);
 
 // Launchers (plan_combine.hip, decode.hip).  They return hipError_t as int.
 int launch_plan(const PlanArgs& a, void* stream);

@@ -21,13 +21,15 @@ Sources (cited by page title and section):
   and "分组潜在注意力机制 GLA" (head groups, each attending its own latent).
 * GQA / MQA sharing: the [MLRA] page's list of cache-reduction methods.
 
-Readings where the pages are silent (each is listed in the design doc):
+Readings where the pages are silent:
 the cache row holds the latent followed by the already rotated RoPE key; the
 query sits at position L-1 and attends tokens [0, L) with no mask; an empty
 sequence gives out = 0 and lse = -inf; lse is the natural log of the sum of
 exp(scaled score); GLA heads are split into contiguous groups; MLRA shares one
 RoPE key per token and has a RoPE query per branch, with one softmax per
-branch; fp8 is OCP E4M3 with a per-token fp32 scale.
+branch; fp8 is OCP E4M3 with a per-token fp32 scale; with several query
+tokens per sequence (multi-token decode) token i of Q sits at position
+L-Q+i and attends rows [0, L-Q+i] (causal), nothing when that is empty.
 """
 from __future__ import annotations
 
@@ -38,7 +40,7 @@ __all__ = [
     "rope", "e4m3_value", "e4m3_decode",
     "logical_rows", "absorb_query",
     "mla_materialised", "gla_materialised", "mlra_materialised", "shared_kv_attention",
-    "decode_paged",
+    "decode_paged", "decode_paged_tokens",
 ]
 
 
@@ -333,3 +335,29 @@ def decode_paged(variant: str, q_lat, q_rope, k_pool, block_table, seq_lens, *, 
         else:
             raise ValueError(f"unknown variant {variant!r}")
     return out, lse
+
+
+def decode_paged_tokens(variant: str, q_lat, q_rope, k_pool, block_table, seq_lens, *, q_len: int, groups: int,
+                        scale: float, page_size: int, v_pool=None, rope_pool=None, scale_pool=None, d_rope: int = 0,
+                        batches=None, heads=None):
+    """Several query tokens per sequence (mla, mqa): the last ``q_len`` positions of every sequence
+    query the cache at once, token i (position L - q_len + i) attending rows 0 .. L - q_len + i.
+
+    Causal attention restricted to the last q_len positions: token i's result is the one-token
+    decode (decode_paged) over the cache prefix of length max(0, L - q_len + 1 + i), which is that
+    definition written out.  ``q_lat`` / ``q_rope`` hold q_len*H rows per sequence (row i*H + h);
+    out and lse come back in the same row order.
+    """
+    q_lat = np.asarray(q_lat)
+    H = q_lat.shape[1] // q_len
+    lens = np.asarray(seq_lens, np.int64)
+    outs, lses = [], []
+    for i in range(q_len):
+        rows = slice(i * H, (i + 1) * H)
+        qr = None if q_rope is None else np.asarray(q_rope)[:, rows]
+        o, s = decode_paged(variant, q_lat[:, rows], qr, k_pool, block_table, np.maximum(lens - q_len + 1 + i, 0),
+                            groups=groups, scale=scale, page_size=page_size, v_pool=v_pool, rope_pool=rope_pool,
+                            scale_pool=scale_pool, d_rope=d_rope, batches=batches, heads=heads)
+        outs.append(o)
+        lses.append(s)
+    return np.concatenate(outs, axis=1), np.concatenate(lses, axis=1)

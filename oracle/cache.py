@@ -13,7 +13,7 @@ What is appended (sources cited by page title and section):
   shared 576-dim row per token.
 * [GTA-GLA]  the GTA/GLA page (jsbsmhs.com): the large model is served in FP8.
 
-Readings where the pages are silent (listed in the design doc): the new token sits
+Readings where the pages are silent: the new token sits
 at logical position L - 1 of a sequence whose length L already counts it; its
 RoPE key is rotated by that position before it is stored (the [MLRA] reading;
 [MLA-RoPE] section 2.4's "recompute k^R every step" is the other one); RoPE

@@ -49,6 +49,7 @@ class Workload:
     scale: float = 1.0
     shuffle: bool = True
     seed: int = 0
+    q_len: int = 1
 
     def lengths(self) -> np.ndarray:
         if isinstance(self.seq_len, tuple):
@@ -132,6 +133,7 @@ class DecodeInputs:
     rope_pool: torch.Tensor | None      # fp8 only: bf16 [P,page,dr]
     scale_pool: torch.Tensor | None     # fp8 only: f32 [P,page]
     v_pool: torch.Tensor | None         # gqa/mqa: [P,page,G,d]
+    q_len: int = 1                      # query tokens per sequence; q_lat/q_rope then hold q_len*H rows
 
     @property
     def batch(self) -> int:
@@ -143,7 +145,7 @@ class DecodeInputs:
 
     @property
     def rows_per_seq(self) -> int:
-        return self.heads * (self.groups if self.variant == "mlra" else 1)
+        return self.heads * (self.groups if self.variant == "mlra" else self.q_len)
 
     def kv_bytes(self) -> int:
         per = kv_bytes_per_token(self.variant, self.groups, self.d_lat, self.d_rope, self.kv_dtype)
@@ -153,8 +155,9 @@ class DecodeInputs:
 def make_inputs(variant: str, batch: int, heads: int, groups: int, d_lat: int, d_rope: int, seq_lens,
                 *, page_size: int = 64, kv_dtype: str = "bf16", q_dtype: str = "bf16", out_dtype: str = "bf16",
                 scale: float = 1.0, shuffle: bool = True, seed: int = 0, poison: bool = True,
-                max_pages_per_seq: int | None = None, spare_pages: int = 1) -> DecodeInputs:
-    """Draw one seeded decode problem.  All values are N(0,1) in their storage type."""
+                max_pages_per_seq: int | None = None, spare_pages: int = 1, q_len: int = 1) -> DecodeInputs:
+    """Draw one seeded decode problem.  All values are N(0,1) in their storage type.  With q_len > 1
+    (mla, mqa) every sequence has q_len query tokens: q_lat / q_rope hold q_len*H rows, row i*H + h."""
     if variant not in LATENT_VARIANTS + SHARED_VARIANTS:
         raise ValueError(f"unknown variant {variant!r}")
     seq_lens = np.broadcast_to(np.asarray(seq_lens, np.int64), (batch,)).copy()
@@ -166,8 +169,8 @@ def make_inputs(variant: str, batch: int, heads: int, groups: int, d_lat: int, d
             q_lat = normal_tensor(generator(seed, 1), (batch, heads, groups, d_lat), q_dtype)
             q_rope = normal_tensor(generator(seed, 2), (batch, heads, groups, d_rope), q_dtype)
         else:
-            q_lat = normal_tensor(generator(seed, 1), (batch, heads, d_lat), q_dtype)
-            q_rope = normal_tensor(generator(seed, 2), (batch, heads, d_rope), q_dtype)
+            q_lat = normal_tensor(generator(seed, 1), (batch, q_len * heads, d_lat), q_dtype)
+            q_rope = normal_tensor(generator(seed, 2), (batch, q_len * heads, d_rope), q_dtype)
         if kv_dtype == "fp8_e4m3":
             k_pool, scale_pool = fill_pool_e4m3(generator(seed, 3), layout, groups * d_lat, poison=poison)
             rope_pool = fill_pool(generator(seed, 4), layout, (d_rope,), "bf16", poison=poison)
@@ -178,18 +181,19 @@ def make_inputs(variant: str, batch: int, heads: int, groups: int, d_lat: int, d
             raise ValueError("shared-KV variants carry no RoPE segment")
         if kv_dtype == "fp8_e4m3":
             raise ValueError("the fp8 cache path covers the latent variants")
-        q_lat = normal_tensor(generator(seed, 1), (batch, heads, d_lat), q_dtype)
+        q_lat = normal_tensor(generator(seed, 1), (batch, q_len * heads, d_lat), q_dtype)
         k_pool = fill_pool(generator(seed, 3), layout, (groups, d_lat), kv_dtype, poison=poison)
         if variant != "gta":
             v_pool = fill_pool(generator(seed, 5), layout, (groups, d_lat), kv_dtype, poison=poison)
     return DecodeInputs(variant=variant, heads=heads, groups=groups, d_lat=d_lat, d_rope=d_rope, scale=float(scale),
                         layout=layout, kv_dtype=kv_dtype, q_dtype=q_dtype, out_dtype=out_dtype, q_lat=q_lat,
-                        q_rope=q_rope, k_pool=k_pool, rope_pool=rope_pool, scale_pool=scale_pool, v_pool=v_pool)
+                        q_rope=q_rope, k_pool=k_pool, rope_pool=rope_pool, scale_pool=scale_pool, v_pool=v_pool,
+                        q_len=q_len)
 
 
 def make_workload_inputs(w: Workload, **overrides) -> DecodeInputs:
     kw = dict(page_size=w.page_size, kv_dtype=w.kv_dtype, q_dtype=w.q_dtype, out_dtype=w.out_dtype,
-              scale=w.scale, shuffle=w.shuffle, seed=w.seed)
+              scale=w.scale, shuffle=w.shuffle, seed=w.seed, q_len=w.q_len)
     kw.update(overrides)
     lens = kw.pop("seq_lens", None)
     batch = kw.pop("batch", w.batch)

@@ -21,7 +21,7 @@ def run_gpu(inp: synth.DecodeInputs, num_splits: int = 0, block_table=None, seq_
     out, lse = lkd.latent_decode(to_dev(inp.q_lat), to_dev(inp.q_rope), k, bt, sl, variant=inp.variant,
                                  scale=inp.scale, groups=inp.groups, v=to_dev(inp.v_pool), rope=to_dev(inp.rope_pool),
                                  kscale=to_dev(inp.scale_pool), num_splits=num_splits,
-                                 out_dtype=out_dtype or inp.out_dtype)
+                                 out_dtype=out_dtype or inp.out_dtype, q_len=inp.q_len)
     torch.cuda.synchronize()
     return out.double().cpu().numpy(), lse.double().cpu().numpy()
 
@@ -29,6 +29,12 @@ def run_gpu(inp: synth.DecodeInputs, num_splits: int = 0, block_table=None, seq_
 def run_oracle(inp: synth.DecodeInputs, batches=None, heads=None):
     f64 = lambda t: None if t is None else t.double().numpy()  # noqa: E731
     k = inp.k_pool.numpy() if inp.kv_dtype == "fp8_e4m3" else f64(inp.k_pool)
+    if inp.q_len > 1:
+        return oracle.decode_paged_tokens(inp.variant, f64(inp.q_lat), f64(inp.q_rope), k, inp.layout.block_table,
+                                          inp.layout.seq_lens, q_len=inp.q_len, groups=inp.groups, scale=inp.scale,
+                                          page_size=inp.layout.page_size, v_pool=f64(inp.v_pool),
+                                          rope_pool=f64(inp.rope_pool), scale_pool=f64(inp.scale_pool),
+                                          d_rope=inp.d_rope, batches=batches, heads=heads)
     return oracle.decode_paged(inp.variant, f64(inp.q_lat), f64(inp.q_rope), k, inp.layout.block_table,
                                inp.layout.seq_lens, groups=inp.groups, scale=inp.scale,
                                page_size=inp.layout.page_size, v_pool=f64(inp.v_pool), rope_pool=f64(inp.rope_pool),

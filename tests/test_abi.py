@@ -22,7 +22,7 @@ def test_library_exports_every_declared_function():
     assert len(names) >= 8
     for n in names:
         assert hasattr(L, n), n
-    assert L.ld_abi_version() == 1
+    assert L.ld_abi_version() == 2
 
 
 def test_status_strings():
@@ -37,7 +37,8 @@ def test_status_strings():
     dict(variant="gta", heads=64, groups=8, d_latent=128, d_rope=0), dict(kv_dtype="fp8_e4m3"),
     dict(variant="gla", groups=2, d_latent=256, kv_dtype="fp8_e4m3"),
     dict(heads=16, d_latent=64, d_rope=16, q_dtype="f32", kv_dtype="f32", out_dtype="f32"),
-    dict(out_dtype="f32"), dict(batch=0), dict(num_splits=7)])
+    dict(out_dtype="f32"), dict(batch=0), dict(num_splits=7), dict(q_len=2), dict(q_len=16),
+    dict(variant="mqa", heads=64, d_latent=512, d_rope=0, q_len=3), dict(q_len=2, kv_dtype="fp8_e4m3")])
 def test_supported_problems_check_ok(kw):
     p = mla(**kw)
     assert lkd.check_problem(p) == OK
@@ -53,9 +54,17 @@ def test_supported_problems_check_ok(kw):
     (dict(variant="gqa", heads=64, groups=8, d_latent=128, d_rope=0, kv_dtype="fp8_e4m3"), DTYPE),
     (dict(d_latent=384), UNSUP), (dict(d_rope=32), UNSUP), (dict(heads=256), UNSUP),
     (dict(q_dtype="f32", kv_dtype="f32", out_dtype="f32"), UNSUP),
+    (dict(q_len=0), SHAPE), (dict(q_len=17), SHAPE), (dict(variant="gla", groups=2, d_latent=256, q_len=2), UNSUP),
+    (dict(variant="mlra", groups=4, d_latent=128, q_len=2), UNSUP),
+    (dict(variant="gqa", heads=64, groups=8, d_latent=128, d_rope=0, q_len=2), UNSUP),
 ])
 def test_bad_problems_rejected(kw, status):
     assert lkd.check_problem(mla(**kw)) == status
+
+
+def test_workspace_grows_with_query_tokens():
+    # partial blocks and combine pieces per unit scale with the query tokens (one work group each)
+    assert lkd.workspace_size(mla(q_len=4)) > lkd.workspace_size(mla(q_len=1))
 
 
 def test_struct_size_guard():

@@ -245,6 +245,38 @@ def test_fused_plan_matches_staged_plan(variant, H, G, d, dr, lens, splits, kv):
     assert not torch.isnan(fused.out).any()
 
 
+# --- several query tokens per sequence (multi-token / speculative decode, MLA and MQA): sequences
+# shorter than q_len (their first tokens see no row), one-, two- and many-stage units, forced
+# splits, 64 heads, an fp8 cache, large MQA head dims; the staged path gives the fused path's bits
+@pytest.mark.parametrize("variant,H,d,dr,lens,Q,splits,kv", [
+    ("mla", 128, 512, 64, [1, 2, 3, 700, 2049], 2, 0, "bf16"),
+    ("mla", 128, 512, 64, [4, 130, 5000], 4, 0, "bf16"),
+    ("mla", 128, 512, 64, [300, 3000], 3, 5, "bf16"),
+    ("mla", 64, 512, 64, [97, 1500], 2, 0, "bf16"),
+    ("mla", 128, 512, 64, [2, 900], 2, 0, "fp8_e4m3"),
+    ("mqa", 64, 128, 0, [5, 1025], 3, 0, "bf16"),
+    ("mqa", 64, 512, 0, [64, 777], 2, 0, "bf16"),
+])
+def test_multi_token_decode(variant, H, d, dr, lens, Q, splits, kv):
+    import latent_kv_cache_absorbed_amd as lkd
+    from gpu_util import to_dev
+    inp = synth.make_inputs(variant, len(lens), H, 1, d, dr, lens, scale=1 / math.sqrt(d + dr), seed=25,
+                            kv_dtype=kv, q_len=Q)
+    _check(inp, num_splits=splits)
+    bt = torch.from_numpy(inp.layout.block_table).cuda()
+    sl = torch.from_numpy(inp.layout.seq_lens).cuda()
+    mk = lambda: lkd.Decoder(to_dev(inp.q_lat), to_dev(inp.q_rope), to_dev(inp.k_pool), bt, sl,  # noqa: E731
+                             variant=variant, scale=inp.scale, v=to_dev(inp.v_pool), rope=to_dev(inp.rope_pool),
+                             kscale=to_dev(inp.scale_pool), num_splits=splits, q_len=Q)
+    fused, staged = mk(), mk()
+    fused.run()
+    staged.plan()
+    staged.decode()
+    staged.combine()
+    torch.cuda.synchronize()
+    assert torch.equal(fused.out, staged.out) and torch.equal(fused.lse, staged.lse)
+
+
 # --- the device planner (ld_plan's kernel and the decode kernel's fused prologue) against the host
 # planner ld_plan_host: unit count and chunk (header words 0 and 1, at the start of the workspace)
 # and every unit record (from byte 256), for batches within one wave of lengths, above it (the

@@ -447,3 +447,72 @@ def test_bytes_per_token_fixed_by_the_pages():
     gta = synth.kv_bytes_per_token("gta", 8, 128, 0, "bf16")
     assert gta == items["GTA cache relative to GQA"]["value"] * gqa
     assert synth.kv_bytes_per_token("gla", 2, 256, 64, "fp8_e4m3") == 512 + 128 + 4
+
+
+# ------------------------------------------------------------------------------------------------
+# several query tokens per sequence (multi-token decode): causal attention over the last positions
+# ------------------------------------------------------------------------------------------------
+def _tokens_inputs(variant, lens, q_len, seed):
+    G, d, dr = (1, 24, 8) if variant == "mla" else (1, 16, 0)
+    return synth.make_inputs(variant, len(lens), 3, G, d, dr, lens, scale=0.3, seed=seed, q_dtype="f32",
+                             kv_dtype="f32", out_dtype="f32", page_size=8, q_len=q_len)
+
+
+def _tokens_oracle(inp):
+    f64 = lambda t: None if t is None else t.double().numpy()  # noqa: E731
+    return oracle.decode_paged_tokens(inp.variant, f64(inp.q_lat), f64(inp.q_rope), f64(inp.k_pool),
+                                      inp.layout.block_table, inp.layout.seq_lens, q_len=inp.q_len, groups=1,
+                                      scale=inp.scale, page_size=inp.layout.page_size, v_pool=f64(inp.v_pool),
+                                      d_rope=inp.d_rope)
+
+
+@pytest.mark.parametrize("variant", ["mla", "mqa"])
+def test_tokens_match_causal_sdpa(variant):
+    """Every (token, head) row against torch's attention over the whole sequence with a causal mask
+    whose last q_len query positions are the tokens."""
+    Q, lens = 3, [9, 20, 3]
+    inp = _tokens_inputs(variant, lens, Q, 41)
+    out, lse = _tokens_oracle(inp)
+    H, d = inp.heads, inp.d_lat
+    for b, L in enumerate(lens):
+        rows = oracle.logical_rows(inp.k_pool.double().numpy(), inp.layout.block_table[b], L, inp.layout.page_size)
+        if variant == "mla":
+            K, V = rows, rows[:, :d]
+            q = np.concatenate([inp.q_lat[b].double().numpy(), inp.q_rope[b].double().numpy()], axis=1)
+        else:
+            K = rows[:, 0, :]
+            V = oracle.logical_rows(inp.v_pool.double().numpy(), inp.layout.block_table[b], L,
+                                    inp.layout.page_size)[:, 0, :]
+            q = inp.q_lat[b].double().numpy()
+        pos = np.repeat(np.arange(L - Q, L), H)           # row i*H + h sits at position L - Q + i
+        mask = np.arange(L)[None, :] <= pos[:, None]
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            torch.tensor(q)[None], torch.tensor(K)[None], torch.tensor(V)[None],
+            attn_mask=torch.tensor(mask)[None], scale=inp.scale)[0].numpy()
+        np.testing.assert_allclose(out[b], ref, rtol=1e-12, atol=1e-13)
+        s = np.where(mask, (q @ K.T) * inp.scale, -np.inf)
+        np.testing.assert_allclose(lse[b], torch.logsumexp(torch.tensor(s), dim=1).numpy(), rtol=1e-13)
+
+
+def test_tokens_one_is_the_single_token_decode():
+    inp = _tokens_inputs("mla", [7, 30], 1, 42)
+    f64 = lambda t: t.double().numpy()  # noqa: E731
+    o1, l1 = _tokens_oracle(inp)
+    o2, l2 = oracle.decode_paged("mla", f64(inp.q_lat), f64(inp.q_rope), f64(inp.k_pool), inp.layout.block_table,
+                                 inp.layout.seq_lens, groups=1, scale=inp.scale, page_size=inp.layout.page_size,
+                                 d_rope=inp.d_rope)
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(l1, l2)
+
+
+def test_tokens_before_the_first_row_see_nothing():
+    """A sequence shorter than q_len: its first tokens have no visible row (out 0, lse -inf); the
+    first token that sees one row returns that row's value."""
+    Q = 4
+    inp = _tokens_inputs("mla", [2, 12], Q, 43)
+    out, lse = _tokens_oracle(inp)
+    H, d = inp.heads, inp.d_lat
+    assert np.all(out[0, : 2 * H] == 0) and np.all(lse[0, : 2 * H] == -np.inf)
+    row0 = oracle.logical_rows(inp.k_pool.double().numpy(), inp.layout.block_table[0], 1, inp.layout.page_size)[0]
+    np.testing.assert_allclose(out[0, 2 * H: 3 * H], np.broadcast_to(row0[:d], (H, d)), rtol=1e-14)
+    assert np.all(np.isfinite(lse[1]))
