@@ -24,6 +24,7 @@ from __future__ import annotations
 
 import argparse
 import csv
+import functools
 import hashlib
 import json
 import os
@@ -93,15 +94,18 @@ def cpu_baseline(inp, budget_s: float):
               rope_pool=f64(inp.rope_pool), scale_pool=f64(inp.scale_pool), d_rope=inp.d_rope)
     B = inp.batch
     lens = inp.layout.seq_lens.astype(np.int64)
+    run = oracle.decode_paged
+    if inp.q_len > 1:
+        run = functools.partial(oracle.decode_paged_tokens, q_len=inp.q_len)
     t0 = time.perf_counter()
-    oracle.decode_paged(*args, batches=[0], **kw)
+    run(*args, batches=[0], **kw)
     t1 = time.perf_counter() - t0
     n = int(max(1, min(B, budget_s / max(t1, 1e-3))))
     batches = list(range(n))
     reps, toks = 0, 0
     t0 = time.perf_counter()
     while True:
-        oracle.decode_paged(*args, batches=batches, **kw)
+        run(*args, batches=batches, **kw)
         reps += 1
         toks += int(lens[:n].sum())
         dt = time.perf_counter() - t0
@@ -242,7 +246,7 @@ def main() -> int:
     first = None
     for (k, v, r, s) in copies:
         d = lkd.Decoder(q_lat, q_rope, k, bt, sl, variant=w.variant, scale=w.scale, groups=w.groups, v=v, rope=r,
-                        kscale=s, num_splits=args.num_splits,
+                        kscale=s, num_splits=args.num_splits, q_len=w.q_len,
                         out=None if first is None else first.out, lse=None if first is None else first.lse,
                         workspace=None if first is None else first.workspace)
         first = first or d
@@ -376,7 +380,9 @@ def main() -> int:
         0 if inp.q_rope is None else inp.q_rope.numel() * inp.q_rope.element_size())
     out_el = 4 if inp.out_dtype == "f32" else 2
     out_bytes = inp.batch * inp.rows_per_seq * (inp.d_v * out_el + 4)
-    flops = inp.heads * int(lens.sum()) * flops_per_token_head(w)
+    # query token i of Q sees the first L - Q + 1 + i rows
+    seen = sum(int(np.maximum(lens - inp.q_len + 1 + i, 0).sum()) for i in range(inp.q_len))
+    flops = inp.heads * seen * flops_per_token_head(w)
     dec_alg_bytes = kv_bytes + q_bytes              # what the decode kernel must read
     achieved = dec_alg_bytes / (dec_ms * 1e-3) / 1e9
     mfma_peak = MFMA_F32_PEAK_TFLOPS if inp.kv_dtype == "f32" else MFMA_BF16_PEAK_TFLOPS
@@ -399,9 +405,9 @@ def main() -> int:
         "config": {"workload": args.workload, "variant": w.variant, "batch": inp.batch, "heads": inp.heads,
                    "groups": inp.groups, "d_latent": inp.d_lat, "d_rope": inp.d_rope,
                    "seq_len": int(lens.max()) if lens.min() == lens.max() else [int(lens.min()), int(lens.max())],
-                   "total_cached_tokens": int(lens.sum()), "page_size": inp.layout.page_size,
+                   "total_cached_tokens": int(lens.sum()), "page_size": inp.layout.page_size, "q_len": inp.q_len,
                    "kv_dtype": inp.kv_dtype, "cache_copies": len(decs), "num_splits": args.num_splits},
-        "tokens_per_s": round(inp.batch / t, 1),
+        "tokens_per_s": round(inp.batch * inp.q_len / t, 1),
         "kv_tokens_per_s": round(float(lens.sum()) / t, 1),
         "hbm_frac_step": round((kv_bytes + q_bytes + out_bytes) / t / 1e9 / HBM_PEAK_GBS, 4),
         "stage_ms": {"plan": round(plan_ms, 5), "decode": round(dec_ms, 5), "combine": round(comb_ms, 5),

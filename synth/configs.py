@@ -83,6 +83,9 @@ WORKLOADS = {
     "gqa_b32_l32k": Workload("gqa_b32_l32k", "gqa", 32, 64, 8, 128, 0, 32768, scale=_S128, seed=4),
     "mqa_b32_l32k": Workload("mqa_b32_l32k", "mqa", 32, 64, 1, 128, 0, 32768, scale=_S128, seed=4),
     "gta_b32_l32k": Workload("gta_b32_l32k", "gta", 32, 64, 8, 128, 0, 32768, scale=_S128, seed=4),
+    # speculative decode over the DeepSeek-V3-shaped batch: two and four query tokens per sequence
+    "mla_q2_b64_l4k": Workload("mla_q2_b64_l4k", "mla", 64, 128, 1, 512, 64, 4096, scale=_S192, seed=2, q_len=2),
+    "mla_q4_b64_l4k": Workload("mla_q4_b64_l4k", "mla", 64, 128, 1, 512, 64, 4096, scale=_S192, seed=2, q_len=4),
     # one kv head of a large head dim (the MFA-style cache: MQA with d >> 128)
     "mqa_d512_b32_l32k": Workload("mqa_d512_b32_l32k", "mqa", 32, 64, 1, 512, 0, 32768,
                                   scale=1.0 / math.sqrt(512.0), seed=4),
