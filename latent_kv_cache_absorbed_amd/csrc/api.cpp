@@ -25,23 +25,13 @@ struct Shape {
 Shape launch_shape(const ld_problem& p) {
   Shape s;
   const int H = p.num_q_heads, G = p.num_groups;
-  if (p.q_len > 1) {
-    // one work group per query token (the tokens take the place of sets): one-set kernels only
-    s.heads_per_set = H;
-    s.hblocks = (H + 31) / 32;
-    if (decode_instantiated(p, 1, s.hblocks)) {
-      s.nsets = 1;
-      s.wg_per_unit = p.q_len;
-    }
-    return s;
-  }
   s.heads_per_set = p.variant == LD_VARIANT_MLRA ? H : H / G;
   s.hblocks = (s.heads_per_set + 31) / 32;
   for (int n = 8; n >= 1; n >>= 1) {
     if (G % n) continue;
     if (!decode_instantiated(p, n, s.hblocks)) continue;
     s.nsets = n;
-    s.wg_per_unit = G / n;
+    s.wg_per_unit = G / n * p.q_len;  // (several query tokens: a group of work groups per token)
     break;
   }
   return s;
@@ -95,8 +85,8 @@ int32_t rows_per_seq(const ld_problem& p) {
   return p.variant == LD_VARIANT_MLRA ? p.num_q_heads * p.num_groups : p.num_q_heads;
 }
 
-// Sets of query rows (their partial blocks and combine pieces): groups, or the query tokens
-int32_t query_sets(const ld_problem& p) { return p.q_len > 1 ? p.q_len : p.num_groups; }
+// Sets of query rows (their partial blocks and combine pieces): the groups of every query token
+int32_t query_sets(const ld_problem& p) { return p.q_len * p.num_groups; }
 
 // Units the automatic planner aims for: one wave of work groups over the chip, i.e. as many work
 // groups per CU as can be resident at once (at most 4; several for the small work groups of the
@@ -163,7 +153,7 @@ int32_t ld_check_problem(const ld_problem* p) {
   if ((long long)p->max_pages_per_seq * p->page_size > 0x7fffffffLL) return LD_ERR_BAD_SHAPE;
   if (p->num_splits < 0) return LD_ERR_BAD_SHAPE;
   if (p->q_len < 1 || p->q_len > 16) return LD_ERR_BAD_SHAPE;
-  if (p->q_len > 1 && p->variant != LD_VARIANT_MLA && p->variant != LD_VARIANT_MQA) return LD_ERR_UNSUPPORTED;
+  if (p->q_len > 1 && p->variant == LD_VARIANT_MLRA) return LD_ERR_UNSUPPORTED;
   if (!std::isfinite(p->softmax_scale) || !(p->softmax_scale > 0.f)) return LD_ERR_BAD_SHAPE;
   const int H = p->num_q_heads, G = p->num_groups;
   switch (p->variant) {
@@ -327,7 +317,7 @@ DecodeArgs decode_args(const ld_problem* p, const WsLayout& w, void* workspace) 
   a.max_multi = w.max_multi;
   a.xblocks = w.xblocks;
   a.batch = p->batch;
-  a.heads = p->num_q_heads * (p->q_len > 1 ? p->q_len : 1);
+  a.heads = p->num_q_heads * p->q_len;
   a.groups = query_sets(*p);
   a.qlen = p->q_len;
   a.cache_groups = p->num_groups;

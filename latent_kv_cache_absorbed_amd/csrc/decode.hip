@@ -294,15 +294,18 @@ __global__ __launch_bounds__(NSETS* HB* SPLIT * 64) void decode_kernel(DecodeArg
     nsplit = a.seqs[4 * b];
   }
 
-  const int set0 = sb * NSETS;
+  // Work group sb of a unit serves query token qi = sb / wpt and the cache sets (latent slices /
+  // kv heads) [lset0, lset0 + NSETS); its query rows form the sets qi * cache_groups + lset0 + s.
+  // Token qi (of qlen) sees the first L_b - qlen + 1 + qi cache rows.
+  const int wpt = a.wg_per_unit / a.qlen;  // work groups per query token
+  const int qi = sb / wpt;
+  const int lset0 = (sb - qi * wpt) * NSETS;
+  const int set0 = qi * a.cache_groups + lset0;
   const int G = a.groups;
-  // several query tokens per sequence: the work group's set is its token, which sees the first
-  // L_b - qlen + 1 + set0 cache rows; every token reads the cache's one latent / kv head
   if (a.qlen > 1) {
     const int Lb = clampi(a.seq_lens[b], 0, a.max_pages * a.page_size);
-    t_end = max(t_begin, min(t_end, Lb - a.qlen + 1 + set0));
+    t_end = max(t_begin, min(t_end, Lb - a.qlen + 1 + qi));
   }
-  const int lset0 = a.qlen > 1 ? 0 : set0;  // first cache set (latent slice / kv head) read
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform, kept in an SGPR
   const int lane = threadIdx.x & 63;
   const int h = lane >> 5;

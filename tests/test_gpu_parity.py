@@ -258,16 +258,32 @@ def test_fused_plan_matches_staged_plan(variant, H, G, d, dr, lens, splits, kv):
     ("mqa", 64, 512, 0, [64, 777], 2, 0, "bf16"),
 ])
 def test_multi_token_decode(variant, H, d, dr, lens, Q, splits, kv):
+    _multi_token_case(variant, H, 1, d, dr, lens, Q, splits, kv)
+
+
+# the grouped variants: each token's rows span all groups (row i*H + h, group h / (H/G))
+@pytest.mark.parametrize("variant,H,G,d,dr,lens,Q,splits,kv", [
+    ("gla", 128, 2, 256, 64, [1, 300, 2049], 2, 0, "bf16"),
+    ("gla", 128, 2, 256, 64, [3, 1111], 3, 4, "fp8_e4m3"),
+    ("gla", 128, 4, 256, 64, [70, 900], 2, 0, "bf16"),
+    ("gqa", 64, 8, 128, 0, [2, 500, 1025], 3, 0, "bf16"),
+    ("gta", 64, 8, 128, 0, [40, 700], 2, 0, "bf16"),
+])
+def test_multi_token_decode_grouped(variant, H, G, d, dr, lens, Q, splits, kv):
+    _multi_token_case(variant, H, G, d, dr, lens, Q, splits, kv)
+
+
+def _multi_token_case(variant, H, G, d, dr, lens, Q, splits, kv):
     import latent_kv_cache_absorbed_amd as lkd
     from gpu_util import to_dev
-    inp = synth.make_inputs(variant, len(lens), H, 1, d, dr, lens, scale=1 / math.sqrt(d + dr), seed=25,
+    inp = synth.make_inputs(variant, len(lens), H, G, d, dr, lens, scale=1 / math.sqrt(d + dr), seed=25,
                             kv_dtype=kv, q_len=Q)
     _check(inp, num_splits=splits)
     bt = torch.from_numpy(inp.layout.block_table).cuda()
     sl = torch.from_numpy(inp.layout.seq_lens).cuda()
     mk = lambda: lkd.Decoder(to_dev(inp.q_lat), to_dev(inp.q_rope), to_dev(inp.k_pool), bt, sl,  # noqa: E731
-                             variant=variant, scale=inp.scale, v=to_dev(inp.v_pool), rope=to_dev(inp.rope_pool),
-                             kscale=to_dev(inp.scale_pool), num_splits=splits, q_len=Q)
+                             variant=variant, scale=inp.scale, groups=G, v=to_dev(inp.v_pool),
+                             rope=to_dev(inp.rope_pool), kscale=to_dev(inp.scale_pool), num_splits=splits, q_len=Q)
     fused, staged = mk(), mk()
     fused.run()
     staged.plan()
