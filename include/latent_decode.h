@@ -30,7 +30,7 @@
  *   GTA   GQA whose V is the same tied state as K (GTA/GLA article, section on
  *         Grouped-Tied Attention).
  *
- * Several query tokens (q_len = Q > 1, all variants but MLRA): every query row r becomes Q
+ * Several query tokens (q_len = Q > 1): every query row r becomes Q
  * rows (i, r), i = 0 .. Q-1, token i seeing the first L_b - Q + 1 + i cache rows
  * (none when that is not positive: out = 0, lse = -inf); the layouts below then
  * have Q*H rows per sequence where they have H, row i*H + h.
@@ -127,7 +127,7 @@ typedef struct ld_problem {
   int32_t num_splits;        /* 0: the planner splits long sequences over CUs; n >= 1: at most n splits,
                                 except that no split spans more than 512 pages */
   int32_t q_len;             /* Q >= 1 query tokens per sequence (several for speculative / multi-token
-                                decode; every variant but MLRA, Q <= 16): query token i sits at position
+                                decode; Q <= 16): query token i sits at position
                                 L_b - Q + i and attends the cache rows 0 .. L_b - Q + i (causal) */
 } ld_problem;
 

@@ -197,13 +197,14 @@ class Decoder:
         out_dtype = out_dtype or ("f32" if q_dtype == "f32" else "bf16")
         self.problem = make_problem(variant, B, H, G, d, dr, k.shape[1], k.shape[0], block_table.shape[1], q_dtype,
                                     kv_dtype, out_dtype, scale, num_splits, q_len)
-        rows = H * G if variant == "mlra" else H * max(q_len, 1)
+        rows = (H * G if variant == "mlra" else H) * max(q_len, 1)
+        Hq = H * max(q_len, 1)
         odt = torch.float32 if out_dtype == "f32" else torch.bfloat16
         dev = q_latent.device
         if out is None:
-            out = torch.empty((B, H, G, d) if variant == "mlra" else (B, rows, d), dtype=odt, device=dev)
+            out = torch.empty((B, Hq, G, d) if variant == "mlra" else (B, rows, d), dtype=odt, device=dev)
         if lse is None:
-            lse = torch.empty((B, H, G) if variant == "mlra" else (B, rows), dtype=torch.float32, device=dev)
+            lse = torch.empty((B, Hq, G) if variant == "mlra" else (B, rows), dtype=torch.float32, device=dev)
         _need(out, "out", (odt,))
         _need(lse, "lse", (torch.float32,))
         if out.numel() != B * rows * d or lse.numel() != B * rows:

@@ -81,8 +81,7 @@ WsLayout ws_layout(const ld_problem& p, int num_cus) {
 }  // namespace
 
 int32_t rows_per_seq(const ld_problem& p) {
-  if (p.q_len > 1) return p.q_len * p.num_q_heads;
-  return p.variant == LD_VARIANT_MLRA ? p.num_q_heads * p.num_groups : p.num_q_heads;
+  return p.q_len * (p.variant == LD_VARIANT_MLRA ? p.num_q_heads * p.num_groups : p.num_q_heads);
 }
 
 // Sets of query rows (their partial blocks and combine pieces): the groups of every query token
@@ -153,7 +152,6 @@ int32_t ld_check_problem(const ld_problem* p) {
   if ((long long)p->max_pages_per_seq * p->page_size > 0x7fffffffLL) return LD_ERR_BAD_SHAPE;
   if (p->num_splits < 0) return LD_ERR_BAD_SHAPE;
   if (p->q_len < 1 || p->q_len > 16) return LD_ERR_BAD_SHAPE;
-  if (p->q_len > 1 && p->variant == LD_VARIANT_MLRA) return LD_ERR_UNSUPPORTED;
   if (!std::isfinite(p->softmax_scale) || !(p->softmax_scale > 0.f)) return LD_ERR_BAD_SHAPE;
   const int H = p->num_q_heads, G = p->num_groups;
   switch (p->variant) {

@@ -316,8 +316,10 @@ __global__ __launch_bounds__(NSETS* HB* SPLIT * 64) void decode_kernel(DecodeArg
   const int gs = set0 + s;
   const int head_in_set = hb * 32 + col;
   const bool valid = head_in_set < a.heads_per_set;
-  const int head = (a.mlra ? 0 : gs * a.heads_per_set) + (valid ? head_in_set : 0);
-  const int row = a.mlra ? head * G + gs : head;
+  // query row of this lane: set gs * heads_per_set + head; MLRA: (token, head, branch), branch innermost
+  const int CGr = a.cache_groups;
+  const int head = (a.mlra ? qi : gs) * a.heads_per_set + (valid ? head_in_set : 0);
+  const int row = a.mlra ? head * CGr + (gs - qi * CGr) : head;
   const int32_t* __restrict__ bt_row = block_table + (size_t)b * a.max_pages;
   const int page_size = a.page_size;
   // The unit's block-table entries (at most kUnitPages) are staged in LDS up front, so that issuing
@@ -411,7 +413,7 @@ __global__ __launch_bounds__(NSETS* HB* SPLIT * 64) void decode_kernel(DecodeArg
   Frag ql[C::KLW];
   Frag qr[C::KRW > 0 ? C::KRW : 1];
   {
-    const size_t qrow = a.mlra ? ((size_t)b * a.heads + head) * G + gs : (size_t)b * a.heads + head;
+    const size_t qrow = a.mlra ? ((size_t)b * a.heads + head) * CGr + (gs - qi * CGr) : (size_t)b * a.heads + head;
     const CT* qlp = static_cast<const CT*>(a.q_lat) + qrow * DL + half * C::KLW * M::KSTEP + h * M::EPL;
     const CT* qrp = static_cast<const CT*>(a.q_rope) + qrow * DR + half * C::KRW * M::KSTEP + h * M::EPL;
     if constexpr (M::EPL == 8) {

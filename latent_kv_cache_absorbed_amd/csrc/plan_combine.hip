@@ -163,12 +163,20 @@ __device__ __forceinline__ PieceGroup piece_group(const DecodeArgs& a, int d_v, 
   return p;
 }
 
+// Output row of query set gs, head head_in_set: gs * heads_per_set + head; MLRA rows are (token,
+// head, branch) with the branch innermost, its sets token * branches + branch
+__device__ __forceinline__ int out_row(const DecodeArgs& a, int gs, int head_in_set) {
+  if (!a.mlra) return gs * a.heads_per_set + head_in_set;
+  const int qi = gs / a.cache_groups;
+  return (qi * a.heads_per_set + head_in_set) * a.cache_groups + (gs - qi * a.cache_groups);
+}
+
 // out and lse of one piece position (lane) of sequence b
 __device__ __forceinline__ void write_piece(const DecodeArgs& a, int d_v, const PieceGroup& p, int b,
                                             const float* o, float lse) {
   if (p.head_in_set >= a.heads_per_set) return;
   const int vals = a.part_bf16 ? 8 : 4;
-  const int row = a.mlra ? p.head_in_set * a.groups + p.gs : p.gs * a.heads_per_set + p.head_in_set;
+  const int row = out_row(a, p.gs, p.head_in_set);
   const size_t orow = (size_t)b * a.rows + row;
   if (p.cb == 0 && p.j == 0 && p.h == 0) a.lse[orow] = lse;
   // value e of piece j is register i = vals * j + e: column 32 cb + 8 (i / 4) + 4 h + i % 4
@@ -258,7 +266,7 @@ __device__ __forceinline__ void write_tile(const DecodeArgs& a, int d_v, const P
     }
   }
   if (p.cb == 0 && p.j == 0 && p.h == 0 && p.head_in_set < a.heads_per_set) {
-    const int row = a.mlra ? p.head_in_set * a.groups + p.gs : p.gs * a.heads_per_set + p.head_in_set;
+    const int row = out_row(a, p.gs, p.head_in_set);
     a.lse[(size_t)b * a.rows + row] = lse;
   }
   __syncthreads();
@@ -267,7 +275,7 @@ __device__ __forceinline__ void write_tile(const DecodeArgs& a, int d_v, const P
   const int head_in_set = p.hb * 32 + r;
   const int col0 = (32 * p.cb) / tcols * tcols;  // first column of the tile
   if (head_in_set < a.heads_per_set) {
-    const int row = a.mlra ? head_in_set * a.groups + p.gs : p.gs * a.heads_per_set + head_in_set;
+    const int row = out_row(a, p.gs, head_in_set);
     const size_t orow = (size_t)b * a.rows + row;
     const float* src = tile + r * (tcols + 1) + ch * (vals == 8 ? 8 : 4);
     if (a.out_bf16) {

@@ -148,7 +148,7 @@ class DecodeInputs:
 
     @property
     def rows_per_seq(self) -> int:
-        return self.heads * (self.groups if self.variant == "mlra" else self.q_len)
+        return self.heads * self.q_len * (self.groups if self.variant == "mlra" else 1)
 
     def kv_bytes(self) -> int:
         per = kv_bytes_per_token(self.variant, self.groups, self.d_lat, self.d_rope, self.kv_dtype)
@@ -169,8 +169,8 @@ def make_inputs(variant: str, batch: int, heads: int, groups: int, d_lat: int, d
     rope_pool = scale_pool = v_pool = q_rope = None
     if variant in LATENT_VARIANTS:
         if variant == "mlra":
-            q_lat = normal_tensor(generator(seed, 1), (batch, heads, groups, d_lat), q_dtype)
-            q_rope = normal_tensor(generator(seed, 2), (batch, heads, groups, d_rope), q_dtype)
+            q_lat = normal_tensor(generator(seed, 1), (batch, q_len * heads, groups, d_lat), q_dtype)
+            q_rope = normal_tensor(generator(seed, 2), (batch, q_len * heads, groups, d_rope), q_dtype)
         else:
             q_lat = normal_tensor(generator(seed, 1), (batch, q_len * heads, d_lat), q_dtype)
             q_rope = normal_tensor(generator(seed, 2), (batch, q_len * heads, d_rope), q_dtype)

@@ -40,7 +40,8 @@ def test_status_strings():
     dict(out_dtype="f32"), dict(batch=0), dict(num_splits=7), dict(q_len=2), dict(q_len=16),
     dict(variant="mqa", heads=64, d_latent=512, d_rope=0, q_len=3), dict(q_len=2, kv_dtype="fp8_e4m3"),
     dict(variant="gla", groups=2, d_latent=256, q_len=2), dict(variant="gqa", heads=64, groups=8, d_latent=128,
-                                                               d_rope=0, q_len=3)])
+                                                               d_rope=0, q_len=3),
+    dict(variant="mlra", groups=4, d_latent=128, q_len=2)])
 def test_supported_problems_check_ok(kw):
     p = mla(**kw)
     assert lkd.check_problem(p) == OK
@@ -56,7 +57,7 @@ def test_supported_problems_check_ok(kw):
     (dict(variant="gqa", heads=64, groups=8, d_latent=128, d_rope=0, kv_dtype="fp8_e4m3"), DTYPE),
     (dict(d_latent=384), UNSUP), (dict(d_rope=32), UNSUP), (dict(heads=256), UNSUP),
     (dict(q_dtype="f32", kv_dtype="f32", out_dtype="f32"), UNSUP),
-    (dict(q_len=0), SHAPE), (dict(q_len=17), SHAPE), (dict(variant="mlra", groups=4, d_latent=128, q_len=2), UNSUP),
+    (dict(q_len=0), SHAPE), (dict(q_len=17), SHAPE),
 ])
 def test_bad_problems_rejected(kw, status):
     assert lkd.check_problem(mla(**kw)) == status

@@ -268,6 +268,8 @@ def test_multi_token_decode(variant, H, d, dr, lens, Q, splits, kv):
     ("gla", 128, 4, 256, 64, [70, 900], 2, 0, "bf16"),
     ("gqa", 64, 8, 128, 0, [2, 500, 1025], 3, 0, "bf16"),
     ("gta", 64, 8, 128, 0, [40, 700], 2, 0, "bf16"),
+    ("mlra", 128, 4, 128, 64, [1, 600, 2000], 2, 0, "bf16"),
+    ("mlra", 128, 1, 128, 64, [5, 1500], 3, 3, "bf16"),
 ])
 def test_multi_token_decode_grouped(variant, H, G, d, dr, lens, Q, splits, kv):
     _multi_token_case(variant, H, G, d, dr, lens, Q, splits, kv)
