@@ -111,8 +111,8 @@ struct DecodeArgs {
   int32_t out_bf16;
   int32_t part_bf16;            // partials stored as bf16 (else f32)
   int32_t mlra;
-  // Several query tokens per sequence (qlen > 1, MLA and MQA): the tokens take the place of sets
-  // (groups = qlen, heads = qlen * H); all read the cache's one latent / kv head (cache_groups = 1),
+  // Several query tokens per sequence (qlen > 1): a unit has wg_per_unit / qlen work groups per
+  // token; the query sets are token x cache set (groups = qlen * cache_groups, heads = qlen * H),
   // token i seeing the first L_b - qlen + 1 + i rows.
   int32_t qlen, cache_groups;
   float scale_log2;             // softmax_scale * log2(e)
