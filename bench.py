@@ -219,7 +219,7 @@ def main() -> int:
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
-              "the decode path is per-GPU and this build has no multi-GPU path.", file=sys.stderr)
+              "the decode path runs on one GPU; there is no multi-GPU path.", file=sys.stderr)
         return 2
 
     import numpy as np
