@@ -186,7 +186,9 @@ int32_t ld_combine_planned(const ld_problem* p, void* out, float* lse, void* wor
  *   lse_r = ln sum_{s<n} exp(partial_lse[r][s])
  *   out_r = sum_{s<n} exp(partial_lse[r][s] - lse_r) * partial_out[r][s][:]
  * Each partial_out[r][s] is that split's normalised output; a split whose lse
- * is -inf has zero weight; n = 0 or all splits empty gives out = 0, lse = -inf.
+ * is -inf has zero weight; n = 0 or all splits empty gives out = 0, lse = -inf;
+ * a NaN lse among a row's splits makes that row's out and lse NaN (as the rule
+ * computes it; the decode's own merge treats its split partials the same way).
  * partial_out f32 [num_rows, max_splits, d_v]; partial_lse f32 [num_rows, max_splits];
  * row_num_splits int32 [num_rows]; out [num_rows, d_v] in out_dtype; lse f32 [num_rows].
  * d_v must be a multiple of 4. */
@@ -201,7 +203,10 @@ int32_t ld_split_kv_combine(int32_t num_rows, int32_t d_v, int32_t max_splits, c
  * cached); the fp8 cache follows the FP8 serving of the GTA/GLA article (jsbsmhs.com).
  *   For sequence b with L = seq_lens[b] >= 1 (the length counting the new token) the token goes to
  *   logical position pos = L - 1: physical page block_table[b*max_pages_per_seq + pos / page_size],
- *   slot pos % page_size.  Sequences with L <= 0 are left alone.
+ *   slot pos % page_size.  A sequence with L <= 0, with L > max_pages_per_seq * page_size, or whose
+ *   block-table entry for that page lies outside [0, num_pages) is skipped: nothing of the cache is
+ *   written for it (unlike the decode, which only reads and clamps, a write must not land in a slot
+ *   the metadata does not name).
  *   c_new   [B, G*d_latent]: the token's latent row (all groups), in q_dtype (F32 or BF16)
  *   kr_new  [B, d_rope]: its RoPE key before rotation, in q_dtype; d_rope must be even
  *   RoPE:   pair (2i, 2i+1) turns by pos * rope_base^(-2i/d_rope) (angle, cosine, sine and rotation

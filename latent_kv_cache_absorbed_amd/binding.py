@@ -17,7 +17,7 @@ import torch
 
 __all__ = [
     "LatentDecodeError", "Decoder", "lib", "library_path", "Problem", "KVCache", "VARIANTS", "DTYPES",
-    "make_problem", "workspace_size", "latent_decode", "split_kv_combine", "validate_metadata", "plan_host",
+    "make_problem", "workspace_size", "latent_decode", "decode_shapes", "split_kv_combine", "validate_metadata", "plan_host",
     "cache_append", "head_projection",
     "check_problem", "status_string", "header_functions",
 ]
@@ -145,6 +145,69 @@ def _need(t, name, dtypes=None):
     return t
 
 
+def decode_shapes(q_latent, q_rope, k, block_table, seq_lens, *, variant: str, groups: int | None = None, v=None,
+                  rope=None, kscale=None, q_len: int = 1):
+    """Check the tensors' shapes against one another (any device) and return (B, H, G, d, d_rope).
+
+    The library reads these buffers on the device with the sizes derived here, so a mismatch (a short
+    seq_lens, a block table with too few rows, a query or pool of the wrong shape) raises ValueError
+    instead of becoming an out-of-bounds read.
+    """
+    if variant not in VARIANTS:
+        raise ValueError(f"unknown variant {variant!r}")
+    if q_len < 1:
+        raise ValueError("q_len must be >= 1")
+    kv_dtype = _TORCH_DTYPE.get(k.dtype)
+    if kv_dtype is None:
+        raise ValueError(f"k has dtype {k.dtype}")
+    latent = variant in ("mla", "gla", "mlra")
+    want_qdim = 4 if variant == "mlra" else 3
+    if q_latent.dim() != want_qdim:
+        raise ValueError(f"q_latent must have {want_qdim} dims for {variant}, has shape {tuple(q_latent.shape)}")
+    B, rows, d = q_latent.shape[0], q_latent.shape[1], q_latent.shape[-1]
+    if rows % q_len:
+        raise ValueError(f"q_latent has {rows} rows per sequence, not a multiple of q_len={q_len}")
+    H = rows // q_len
+    if seq_lens.dim() != 1 or seq_lens.numel() != B:
+        raise ValueError(f"seq_lens has shape {tuple(seq_lens.shape)}, expected [{B}]")
+    if block_table.dim() != 2 or block_table.shape[0] != B or block_table.shape[1] < 1:
+        raise ValueError(f"block_table has shape {tuple(block_table.shape)}, expected [{B}, max_pages_per_seq]")
+    if k.dim() < 3:
+        raise ValueError(f"k has shape {tuple(k.shape)}, expected [num_pages, page_size, ...]")
+    P, page = k.shape[0], k.shape[1]
+    if latent:
+        if q_rope is None or q_rope.dim() != want_qdim:
+            raise ValueError(f"q_rope must have {want_qdim} dims for {variant}")
+        dr = q_rope.shape[-1]
+        if variant == "mlra":
+            G = q_latent.shape[2]
+        elif variant == "mla":
+            G = 1
+        else:
+            lat_cols = k.shape[-1] if kv_dtype == "fp8_e4m3" else k.shape[-1] - dr
+            G = groups if groups is not None else lat_cols // d
+        if tuple(q_rope.shape[:-1]) != tuple(q_latent.shape[:-1]):
+            raise ValueError(f"q_rope has shape {tuple(q_rope.shape)}, q_latent {tuple(q_latent.shape)}")
+        row = G * d if kv_dtype == "fp8_e4m3" else G * d + dr
+        if k.dim() != 3 or k.shape[2] != row:
+            raise ValueError(f"k has shape {tuple(k.shape)}, expected [num_pages, page_size, {row}]")
+        if kv_dtype == "fp8_e4m3":
+            if rope is None or tuple(rope.shape) != (P, page, dr):
+                raise ValueError(f"rope must have shape [{P}, {page}, {dr}]")
+            if kscale is None or tuple(kscale.shape) != (P, page):
+                raise ValueError(f"kscale must have shape [{P}, {page}]")
+    else:
+        dr = 0
+        if k.dim() != 4 or k.shape[3] != d:
+            raise ValueError(f"k has shape {tuple(k.shape)}, expected [num_pages, page_size, kv_heads, {d}]")
+        G = k.shape[2]
+        if variant != "gta" and (v is None or tuple(v.shape) != tuple(k.shape)):
+            raise ValueError(f"v must have k's shape {tuple(k.shape)}")
+    if groups is not None and groups != G:
+        raise ValueError(f"groups={groups} does not match the tensors ({G})")
+    return B, H, G, d, dr
+
+
 class Decoder:
     """A decode problem bound to its device tensors: ``run()`` is one ld_latent_decode call.
 
@@ -168,32 +231,15 @@ class Decoder:
         kv_dtype = _TORCH_DTYPE[k.dtype]
         q_dtype = _TORCH_DTYPE[q_latent.dtype]
         latent = variant in ("mla", "gla", "mlra")
-        B, H = q_latent.shape[0], q_latent.shape[1]
-        d = q_latent.shape[-1]
-        if q_len > 1:  # q_latent holds Q*H rows per sequence, row i*H + h
-            if H % q_len:
-                raise ValueError(f"q_latent has {H} rows per sequence, not a multiple of q_len={q_len}")
-            H //= q_len
         if latent:
             _need(q_rope, "q_rope", (q_latent.dtype,))
-            dr = q_rope.shape[-1]
-            if variant == "mlra":
-                G = q_latent.shape[2]
-            elif variant == "mla":
-                G = 1
-            else:
-                lat_cols = k.shape[-1] if kv_dtype == "fp8_e4m3" else k.shape[-1] - dr
-                G = groups if groups is not None else lat_cols // d
             if kv_dtype == "fp8_e4m3":
                 _need(rope, "rope", (torch.bfloat16,))
                 _need(kscale, "kscale", (torch.float32,))
-        else:
-            dr = 0
-            G = k.shape[2]
-            if variant != "gta":
-                _need(v, "v", (k.dtype,))
-        if groups is not None and groups != G:
-            raise ValueError(f"groups={groups} does not match the tensors ({G})")
+        elif variant != "gta":
+            _need(v, "v", (k.dtype,))
+        B, H, G, d, dr = decode_shapes(q_latent, q_rope, k, block_table, seq_lens, variant=variant, groups=groups,
+                                       v=v, rope=rope, kscale=kscale, q_len=q_len)
         out_dtype = out_dtype or ("f32" if q_dtype == "f32" else "bf16")
         self.problem = make_problem(variant, B, H, G, d, dr, k.shape[1], k.shape[0], block_table.shape[1], q_dtype,
                                     kv_dtype, out_dtype, scale, num_splits, q_len)

@@ -37,6 +37,13 @@ Shape launch_shape(const ld_problem& p) {
   return s;
 }
 
+// Forced splits: the most splits one sequence can get, the requested count or, when a split would
+// span more than kUnitPages pages, ceil(max_pages_per_seq / kUnitPages).
+int32_t forced_split_bound(const ld_problem& p) {
+  const int32_t longest = (p.max_pages_per_seq + kUnitPages - 1) / kUnitPages;
+  return p.num_splits > longest ? p.num_splits : longest;
+}
+
 WsLayout ws_layout(const ld_problem& p, int num_cus) {
   WsLayout w;
   w.max_units = max_units_for(p, num_cus);
@@ -55,8 +62,11 @@ WsLayout ws_layout(const ld_problem& p, int num_cus) {
   w.part_out = off;
   off = round256(off + slots * w.d_v * (p.out_dtype == LD_BF16 ? 2 : 4));
   // combine tasks: a sequence with n > 1 splits is merged in ceil(n / kCombineChunk) chunks (an empty
-  // one in one task), so there are at most max_units / kCombineChunk + B of them
-  w.max_tasks = p.num_splits > 0 ? p.batch * ((p.num_splits + kCombineChunk - 1) / kCombineChunk)
+  // one in one task), so there are at most max_units / kCombineChunk + B of them.  Forced splits: a
+  // sequence gets the requested count, or more when a split would span more than kUnitPages pages,
+  // so the bound takes the larger of the two.
+  const int32_t n_forced = forced_split_bound(p);
+  w.max_tasks = p.num_splits > 0 ? p.batch * ((n_forced + kCombineChunk - 1) / kCombineChunk)
                                  : (w.max_units + kCombineChunk - 1) / kCombineChunk + p.batch;
   const size_t vals = p.out_dtype == LD_BF16 ? 8 : 4;   // values per piece
   const size_t pieces = (size_t)query_sets(p) * launch_shape(p).hblocks * (w.d_v / 32) * (16 / vals) * 64;
@@ -64,7 +74,7 @@ WsLayout ws_layout(const ld_problem& p, int num_cus) {
   w.tasks = off;
   off = round256(off + (size_t)w.max_tasks * 2 * sizeof(int32_t));
   // a sequence merged in more than one chunk has more than kCombineChunk units
-  w.max_multi = p.num_splits > 0 ? (p.num_splits > kCombineChunk ? p.batch : 0)
+  w.max_multi = p.num_splits > 0 ? (n_forced > kCombineChunk ? p.batch : 0)
                                  : std::min<int32_t>(p.batch, w.max_units / (kCombineChunk + 1));
   w.multi = off;
   off = round256(off + (size_t)(w.max_multi > 0 ? w.max_multi : 1) * sizeof(int32_t));
@@ -111,7 +121,7 @@ int32_t max_units_for(const ld_problem& p, int32_t num_cus) {
   const long long longest = (p.max_pages_per_seq + kUnitPages - 1) / kUnitPages;
   long long m;
   if (p.num_splits > 0)
-    m = (long long)p.batch * (p.num_splits > longest ? p.num_splits : longest);
+    m = (long long)p.batch * forced_split_bound(p);
   else
     m = target_units_for(p, num_cus) + (long long)p.batch * longest;
   return (int32_t)(m > (1 << 30) ? (1 << 30) : m);

@@ -48,11 +48,15 @@ template <int KV>
 __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
   __shared__ float red[kAppendThreads / 64];
   const int b = blockIdx.x;
+  // A write goes only where the metadata says the token lives: a length outside [1, capacity] or a
+  // page id outside the pool leaves the cache untouched (clamping would overwrite another slot,
+  // possibly another sequence's).
   const int cap = a.max_pages * a.page_size;
-  const int L = min(max(a.seq_lens[b], 0), cap);
-  if (L < 1) return;
+  const int L = a.seq_lens[b];
+  if (L < 1 || L > cap) return;
   const int pos = L - 1;
-  const int page = min(max(a.block_table[(size_t)b * a.max_pages + pos / a.page_size], 0), a.num_pages - 1);
+  const int page = a.block_table[(size_t)b * a.max_pages + pos / a.page_size];
+  if (page < 0 || page >= a.num_pages) return;
   const size_t slot = (size_t)page * a.page_size + pos % a.page_size;
   const int D = a.d_lat;   // all groups
   const int DR = a.d_rope;

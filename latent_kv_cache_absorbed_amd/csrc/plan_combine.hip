@@ -203,14 +203,22 @@ constexpr int kBatch = 8;
 // 2^-22 (1 + |x|), and weights of large |x| are negligible beside the largest (which is 1)
 __device__ __forceinline__ float wexp(float x) { return __builtin_amdgcn_exp2f(x * 1.44269504088896340736f); }
 
+// A NaN lse (a NaN reached that split's scores, e.g. through a NaN query) makes the merged row NaN,
+// as the combine rule computes it; fmaxf would drop it, so it is recorded by poisoning `tot`, which
+// every later rescale and merge carries along.
 struct Merge {
   float M = -INFINITY, tot = 0.f, o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   template <int KB = kBatch>
   __device__ __forceinline__ void add(const float* ls, const float (*v)[8], int valid, int vals) {
     float bm = -INFINITY;
+    bool nan = false;
 #pragma unroll
     for (int k = 0; k < KB; ++k)
-      if (k < valid) bm = fmaxf(bm, ls[k]);
+      if (k < valid) {
+        bm = fmaxf(bm, ls[k]);
+        nan |= ls[k] != ls[k];
+      }
+    if (nan) tot = __builtin_nanf("");
     const float Mn = fmaxf(M, bm);
     if (Mn == -INFINITY) return;
     const float r = (M == -INFINITY) ? 0.f : wexp(M - Mn);
@@ -229,6 +237,7 @@ struct Merge {
   }
   // fold in another state (its pairs come after this one's)
   __device__ __forceinline__ void merge(float M2, float tot2, const float* o2) {
+    if (tot2 != tot2) tot = __builtin_nanf("");
     const float Mn = fmaxf(M, M2);
     if (Mn == -INFINITY) return;
     const float r1 = (M == -INFINITY) ? 0.f : wexp(M - Mn);
@@ -238,8 +247,13 @@ struct Merge {
     for (int e = 0; e < 8; ++e) o[e] = o[e] * r1 + o2[e] * r2;
     M = Mn;
   }
-  // normalised output and lse (0 and -inf when every lse was -inf)
+  // normalised output and lse (0 and -inf when every lse was -inf; NaN when one was NaN)
   __device__ __forceinline__ float finish() {
+    if (tot != tot) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = __builtin_nanf("");
+      return __builtin_nanf("");
+    }
     if (M == -INFINITY) return -INFINITY;
     const float inv = 1.f / tot;
 #pragma unroll
@@ -414,9 +428,14 @@ __global__ __launch_bounds__(kSeqWaves * 64) void combine_seq_kernel(DecodeArgs 
     }
     // one online-merge step over the whole chunk, each piece converted as it is folded in
     float bm = -INFINITY;
+    bool nan = false;
 #pragma unroll
     for (int k = 0; k < kCombineChunk; ++k)
-      if (k < cnt) bm = fmaxf(bm, ls[k]);
+      if (k < cnt) {
+        bm = fmaxf(bm, ls[k]);
+        nan |= ls[k] != ls[k];
+      }
+    if (nan) m.tot = __builtin_nanf("");
     const float Mn = fmaxf(m.M, bm);
     if (Mn != -INFINITY) {
       const float r = (m.M == -INFINITY) ? 0.f : wexp(m.M - Mn);
@@ -492,10 +511,18 @@ __global__ __launch_bounds__(kCombineThreads) void combine_rows_kernel(int num_r
     const int n = clampi(nsplits[r], 0, max_splits);
     const float* ls = part_lse + (size_t)r * max_splits;
     float M = -INFINITY;
-    for (int s = 0; s < n; ++s) M = fmaxf(M, ls[s]);
+    bool nan = false;
+    for (int s = 0; s < n; ++s) {
+      M = fmaxf(M, ls[s]);
+      nan |= ls[s] != ls[s];
+    }
     float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
     float lse = -INFINITY;
-    if (M != -INFINITY) {
+    if (nan) {  // a NaN lse makes the row NaN (fmaxf above skips it)
+      const float q = __builtin_nanf("");
+      o = make_float4(q, q, q, q);
+      lse = q;
+    } else if (M != -INFINITY) {
       float tot = 0.f;
       for (int s = 0; s < n; ++s) tot += expf(ls[s] - M);
       lse = M + logf(tot);

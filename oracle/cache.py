@@ -77,22 +77,32 @@ def append_slot(block_table_row, L: int, page_size: int):
     return int(np.asarray(block_table_row)[pos // page_size]), pos % page_size
 
 
-def cache_append(c_new, kr_new, block_table, seq_lens, *, page_size: int, fp8: bool, base: float = 10000.0):
-    """What one append writes, per sequence b with L_b >= 1.
+def cache_append(c_new, kr_new, block_table, seq_lens, *, page_size: int, fp8: bool, base: float = 10000.0,
+                 num_pages: int | None = None):
+    """What one append writes, per sequence b with 1 <= L_b <= capacity.
 
     c_new [B, D] (the new token's latent, all groups), kr_new [B, dr] (its
     un-rotated RoPE key).  Returns a list of dicts with b, page, slot, pos and
     either ``latent`` (fp64 values) or ``codes`` / ``scale`` (fp8), plus
     ``rope`` (the rotated key, fp64).
+
+    Reading (the pages do not treat bad metadata): the token is written only to
+    the slot the metadata names.  A sequence whose length exceeds the block
+    table's capacity (columns x page_size), or whose page entry lies outside
+    the pool [0, num_pages) when ``num_pages`` is given, gets no write.
     """
     c_new = np.asarray(c_new)
     kr_new = np.asarray(kr_new, np.float64)
+    block_table = np.asarray(block_table)
+    capacity = block_table.shape[1] * page_size
     writes = []
     for b in range(c_new.shape[0]):
         L = int(seq_lens[b])
-        if L < 1:
+        if L < 1 or L > capacity:
             continue
         page, slot = append_slot(block_table[b], L, page_size)
+        if num_pages is not None and not 0 <= page < num_pages:
+            continue
         w = {"b": b, "page": page, "slot": slot, "pos": L - 1,
              "rope": rope(kr_new[b], L - 1, base) if kr_new.shape[-1] else np.zeros(0)}
         if fp8:

@@ -147,3 +147,36 @@ def test_append_zero_rows_and_huge_values_fp8():
                                  fp8=True):
         np.testing.assert_array_equal(k[w["page"], w["slot"]].cpu().numpy(), w["codes"])
         assert sc[w["page"], w["slot"]].item() == float(w["scale"])
+
+
+def test_append_skips_invalid_metadata():
+    """A block-table entry outside the pool (-1, num_pages) or a length above the table's capacity writes
+    nothing: every byte of every pool is unchanged, while the valid sequences in the same call are written."""
+    import latent_kv_cache_absorbed_amd as lkd
+    r = np.random.default_rng(9)
+    page, num_pages, max_pages = 64, 6, 2
+    lens = np.array([10, 70, 129, 128, 1], np.int32)    # 129 > capacity 128
+    table = np.array([[-1, 0], [1, 6], [2, 3], [4, 5], [0, 1]], np.int32)   # b0: page -1, b1: page 6
+    dev = torch.device("cuda")
+    for kv in ("bf16", "fp8_e4m3"):
+        c = torch.from_numpy(r.normal(size=(5, 512)).astype(np.float32)).to(torch.bfloat16)
+        kr = torch.from_numpy(r.normal(size=(5, 64)).astype(np.float32)).to(torch.bfloat16)
+        if kv == "fp8_e4m3":
+            k0 = torch.from_numpy(r.integers(0, 0x7F, size=(num_pages, page, 512)).astype(np.uint8))
+            rope0 = torch.from_numpy(r.normal(size=(num_pages, page, 64)).astype(np.float32)).to(torch.bfloat16)
+            sc0 = torch.from_numpy(r.uniform(0.5, 2, size=(num_pages, page)).astype(np.float32))
+        else:
+            k0 = torch.from_numpy(r.normal(size=(num_pages, page, 576)).astype(np.float32)).to(torch.bfloat16)
+            rope0 = sc0 = None
+        k = k0.to(dev)
+        rope = None if rope0 is None else rope0.to(dev)
+        sc = None if sc0 is None else sc0.to(dev)
+        print(f"case append invalid metadata kv={kv} lens={list(lens)}", flush=True)
+        lkd.cache_append(c.to(dev), kr.to(dev), k, torch.from_numpy(table).to(dev), torch.from_numpy(lens).to(dev),
+                         rope=rope, kscale=sc)
+        torch.cuda.synchronize()
+        writes = oracle.cache_append(c.float().numpy(), kr.double().numpy(), table, lens, page_size=page,
+                                     fp8=(kv == "fp8_e4m3"), num_pages=num_pages)
+        assert sorted(w["b"] for w in writes) == [3, 4]       # b0, b1 (bad page) and b2 (too long) skipped
+        after = (k.cpu(), None if rope is None else rope.cpu(), None if sc is None else sc.cpu())
+        _check(writes, (k0, rope0, sc0), after, kv, 512, 64, "bf16")

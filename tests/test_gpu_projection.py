@@ -80,7 +80,7 @@ def test_query_absorption_then_decode_matches_the_materialised_model():
                                          inp.scale)
         rel = np.max(np.abs(o[b] - ref), axis=1) / np.max(np.abs(ref), axis=1)
         print(f"   sequence {b}: max row error {rel.max():.3e}", flush=True)
-        assert rel.max() <= 3e-2     # three bf16 roundings (q_lat, P, o_lat) on the way
+        assert rel.max() <= 1e-2     # bf16 roundings on the way: q_lat, P, o_lat (the up-projection is f32)
 
 
 def test_mlra_branch_sum_as_one_stacked_projection():

@@ -97,3 +97,17 @@ def test_appended_token_is_the_last_row_the_decode_reads():
         np.testing.assert_allclose(last[D:], oracle.rope(kr[b], lens[b] - 1), rtol=0, atol=0)
     # a zero-length sequence writes nothing
     assert len(oracle.cache_append(c, kr, table, np.array([0, 5, 0]), page_size=page, fp8=False)) == 1
+
+
+def test_append_writes_only_where_the_metadata_points():
+    """Lengths above the block table's capacity and page entries outside the pool get no write."""
+    c = np.ones((4, 8))
+    kr = np.zeros((4, 2))
+    table = np.array([[0, 1], [2, -1], [3, 4], [5, 7]], np.int32)
+    lens = np.array([5, 12, 17, 9], np.int32)        # page 4: b1 -> entry -1, b2 -> 17 > 2 * 8, b3 -> 7 >= 6
+    w = oracle.cache_append(c, kr, table, lens, page_size=8, fp8=False, num_pages=6)
+    assert [x["b"] for x in w] == [0]
+    assert (w[0]["page"], w[0]["slot"]) == (0, 4)
+    # without a pool size only the capacity rule applies
+    w = oracle.cache_append(c, kr, table, lens, page_size=8, fp8=False)
+    assert [x["b"] for x in w] == [0, 1, 3]
