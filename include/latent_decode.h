@@ -168,6 +168,27 @@ int32_t ld_latent_decode(const ld_problem* p, const void* q_latent, const void* 
                          const ld_kv_cache* cache, const int32_t* block_table, const int32_t* seq_lens,
                          void* out, float* lse, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Size of the fixed device array that ld_latent_decode_noalloc uses as its workspace (64 MiB). */
+#define LD_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): ld_latent_decode with the workspace taken from a fixed
+ * device array of the library, LD_NOALLOC_SCRATCH_BYTES bytes, instead of a caller buffer.  Same
+ * problem, arguments, layouts, results (the same bits) and errors as ld_latent_decode.
+ *   - It allocates nothing: no hipMalloc/hipFree, no library allocation.  The array is part of the
+ *     library's device code; each GPU the library runs on holds its own copy until the process
+ *     ends.  Its device address is looked up on the first call on each device.
+ *   - A problem whose ld_workspace_size exceeds LD_NOALLOC_SCRATCH_BYTES is rejected with
+ *     LD_ERR_WORKSPACE_TOO_SMALL before anything is queued (every one-token workload of the
+ *     benchmark fits; several query tokens at batch 64 and 128 heads do not).
+ *   - Every call on one GPU shares that GPU's array and leaves its contents behind (the decode
+ *     kernel re-initialises what must start at zero).  Calls that overlap on one GPU -- on two
+ *     streams, or from two threads without ordering -- race on the array: order them on one
+ *     stream, or use ld_latent_decode with a workspace of one's own per stream. */
+int32_t ld_latent_decode_noalloc(const ld_problem* p, const void* q_latent, const void* q_rope,
+                                 const ld_kv_cache* cache, const int32_t* block_table, const int32_t* seq_lens,
+                                 void* out, float* lse, void* stream);
+
 /* Stage-wise form of ld_latent_decode: ld_plan, then ld_decode_planned, then
  * ld_combine_planned, queued on one stream in that order with the same problem
  * shape and workspace.  The plan depends only on seq_lens and the shape, so a

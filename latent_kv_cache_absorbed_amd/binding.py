@@ -18,7 +18,7 @@ import torch
 __all__ = [
     "LatentDecodeError", "Decoder", "lib", "library_path", "Problem", "KVCache", "VARIANTS", "DTYPES",
     "make_problem", "workspace_size", "latent_decode", "decode_shapes", "split_kv_combine", "validate_metadata", "plan_host",
-    "cache_append", "head_projection",
+    "cache_append", "head_projection", "NOALLOC_SCRATCH_BYTES",
     "check_problem", "status_string", "header_functions",
 ]
 
@@ -75,6 +75,8 @@ def lib():
         L.ld_workspace_size.argtypes = [P, ctypes.POINTER(sz)]
         L.ld_latent_decode.restype = i32
         L.ld_latent_decode.argtypes = [P, vp, vp, ctypes.POINTER(KVCache), vp, vp, vp, vp, vp, sz, vp]
+        L.ld_latent_decode_noalloc.restype = i32
+        L.ld_latent_decode_noalloc.argtypes = [P, vp, vp, ctypes.POINTER(KVCache), vp, vp, vp, vp, vp]
         L.ld_plan.restype = i32
         L.ld_plan.argtypes = [P, vp, vp, sz, vp]
         L.ld_decode_planned.restype = i32
@@ -299,6 +301,19 @@ class Decoder:
         if st:
             raise LatentDecodeError(st, "ld_latent_decode")
         return self.out, self.lse
+
+    def run_noalloc(self, stream=None):
+        """ld_latent_decode_noalloc: the same step with the library's fixed device array as workspace
+        (this object's own workspace tensor is not used)."""
+        st = lib().ld_latent_decode_noalloc(ctypes.byref(self.problem), _ptr(self.q_latent), _ptr(self.q_rope),
+                                            ctypes.byref(self.cache), _ptr(self.block_table), _ptr(self.seq_lens),
+                                            _ptr(self.out), _ptr(self.lse), self._stream(stream))
+        if st:
+            raise LatentDecodeError(st, "ld_latent_decode_noalloc")
+        return self.out, self.lse
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20     # LD_NOALLOC_SCRATCH_BYTES
 
 
 def latent_decode(q_latent, q_rope, k, block_table, seq_lens, *, variant: str, scale: float, groups: int | None = None,

@@ -213,3 +213,24 @@ def test_validate_metadata():
     assert lkd.validate_metadata(p, bt, np.array([-1, 0], np.int32)) == META
     bt[0, 0] = -3
     assert lkd.validate_metadata(p, bt, np.array([5, 0], np.int32)) == META
+
+
+def test_noalloc_rejects_oversized_problems_before_touching_the_device():
+    """ld_latent_decode_noalloc checks the problem's workspace against its fixed array first: a problem
+    that needs more returns LD_ERR_WORKSPACE_TOO_SMALL with no device call (so this runs without a GPU)."""
+    import ctypes
+
+    import numpy as np
+
+    import latent_kv_cache_absorbed_amd as lkd
+    p = lkd.make_problem("mla", 64, 128, 1, 512, 64, 64, 4097, 64, "bf16", "bf16", "bf16", 0.07, q_len=4)
+    assert lkd.workspace_size(p) > lkd.NOALLOC_SCRATCH_BYTES
+    buf = np.zeros(1024, np.uint8)
+    base = buf.ctypes.data + (-buf.ctypes.data) % 256
+    ptr = ctypes.c_void_p(base)
+    cache = lkd.KVCache(base, None, None, None)
+    st = lkd.lib().ld_latent_decode_noalloc(ctypes.byref(p), ptr, ptr, ctypes.byref(cache), ptr, ptr, ptr, ptr, None)
+    assert st == 6
+    bad = lkd.make_problem("mla", 1, 128, 2, 512, 64, 64, 4, 4, "bf16", "bf16", "bf16", 0.07)   # MLA with 2 groups
+    assert lkd.lib().ld_latent_decode_noalloc(ctypes.byref(bad), ptr, ptr, ctypes.byref(cache), ptr, ptr, ptr, ptr,
+                                              None) == 2
