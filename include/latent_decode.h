@@ -168,6 +168,16 @@ int32_t ld_latent_decode(const ld_problem* p, const void* q_latent, const void* 
                          const ld_kv_cache* cache, const int32_t* block_table, const int32_t* seq_lens,
                          void* out, float* lse, void* workspace, size_t workspace_bytes, void* stream);
 
+/* The first of ld_latent_decode's two launches: the decode kernel with the planner rule applied in
+ * its own prologue, which leaves the plan arrays in the workspace.  Followed by ld_combine_planned
+ * (same problem, output buffers and workspace, same stream), it is ld_latent_decode, launch for
+ * launch and bit for bit; the split lets a caller put work or a timing event between the decode
+ * and the merge of its split partials (the flash-decoding combine).  Argument checks, ownership and
+ * errors as ld_latent_decode. */
+int32_t ld_plan_decode(const ld_problem* p, const void* q_latent, const void* q_rope, const ld_kv_cache* cache,
+                       const int32_t* block_table, const int32_t* seq_lens, void* out, float* lse, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
 /* Size of the fixed device array that ld_latent_decode_noalloc uses as its workspace (64 MiB). */
 #define LD_NOALLOC_SCRATCH_BYTES (64u << 20)
 

@@ -75,6 +75,8 @@ def lib():
         L.ld_workspace_size.argtypes = [P, ctypes.POINTER(sz)]
         L.ld_latent_decode.restype = i32
         L.ld_latent_decode.argtypes = [P, vp, vp, ctypes.POINTER(KVCache), vp, vp, vp, vp, vp, sz, vp]
+        L.ld_plan_decode.restype = i32
+        L.ld_plan_decode.argtypes = [P, vp, vp, ctypes.POINTER(KVCache), vp, vp, vp, vp, vp, sz, vp]
         L.ld_latent_decode_noalloc.restype = i32
         L.ld_latent_decode_noalloc.argtypes = [P, vp, vp, ctypes.POINTER(KVCache), vp, vp, vp, vp, vp]
         L.ld_plan.restype = i32
@@ -292,6 +294,16 @@ class Decoder:
                                       _ptr(self.workspace), self.ws_bytes, self._stream(stream))
         if st:
             raise LatentDecodeError(st, "ld_combine_planned")
+
+    def plan_decode(self, stream=None):
+        """ld_plan_decode: the first launch of run() (the decode kernel planning for itself); combine()
+        completes the step."""
+        st = lib().ld_plan_decode(ctypes.byref(self.problem), _ptr(self.q_latent), _ptr(self.q_rope),
+                                  ctypes.byref(self.cache), _ptr(self.block_table), _ptr(self.seq_lens),
+                                  _ptr(self.out), _ptr(self.lse), _ptr(self.workspace), self.ws_bytes,
+                                  self._stream(stream))
+        if st:
+            raise LatentDecodeError(st, "ld_plan_decode")
 
     def run(self, stream=None):
         st = lib().ld_latent_decode(ctypes.byref(self.problem), _ptr(self.q_latent), _ptr(self.q_rope),

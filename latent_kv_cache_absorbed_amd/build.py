@@ -19,15 +19,18 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "liblatent_decode.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["api.cpp", "plan_combine.hip", "decode.hip", "append.hip", "projection.hip", "noalloc.hip"]
+SOURCES = ["api.cpp", "plan_combine.hip", "decode.hip", "decode_pipe.hip", "append.hip", "projection.hip",
+           "noalloc.hip"]
 
 COMMON = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-I", INCLUDE, "-I", CSRC,
           # packed fp32 VALU forms are kept out of every kernel
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-Wall", "-Wno-unused-function"]
-# Per-source flags: decode.hip keeps its MFMA accumulators in the VGPR file (at two waves per SIMD
-# this avoids AGPR round trips and spills).
-EXTRA = {"decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+# Per-source flags: the decode kernels keep the results of their builtin MFMAs in the VGPR file (at two
+# waves per SIMD this avoids AGPR round trips and spills; the pipelined kernel's own P.V accumulators
+# sit in AGPRs through inline asm).
+EXTRA = {"decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+         "decode_pipe.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def _compile(src: str, extra) -> str:

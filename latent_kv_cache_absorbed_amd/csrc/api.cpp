@@ -437,9 +437,9 @@ int32_t ld_combine_planned(const ld_problem* p, void* out, float* lse, void* wor
   return launch_combine_ws(a, p->d_latent, stream) == hipSuccess ? LD_OK : LD_ERR_HIP;
 }
 
-int32_t ld_latent_decode(const ld_problem* p, const void* q_latent, const void* q_rope, const ld_kv_cache* cache,
-                         const int32_t* block_table, const int32_t* seq_lens, void* out, float* lse, void* workspace,
-                         size_t workspace_bytes, void* stream) {
+int32_t ld_plan_decode(const ld_problem* p, const void* q_latent, const void* q_rope, const ld_kv_cache* cache,
+                       const int32_t* block_table, const int32_t* seq_lens, void* out, float* lse, void* workspace,
+                       size_t workspace_bytes, void* stream) {
   const int32_t st = ld_check_problem(p);
   if (st != LD_OK) return st;
   if (p->batch == 0) return LD_OK;
@@ -450,9 +450,15 @@ int32_t ld_latent_decode(const ld_problem* p, const void* q_latent, const void* 
   if (sw != LD_OK) return sw;
   // one launch fewer than ld_plan + ld_decode_planned: the decode kernel plans for itself and
   // leaves the plan arrays in the workspace for the combine
-  const int32_t r = decode_launch(p, w, q_latent, q_rope, cache, block_table, seq_lens, out, lse, workspace, true,
-                                  stream);
-  if (r != LD_OK) return r;
+  return decode_launch(p, w, q_latent, q_rope, cache, block_table, seq_lens, out, lse, workspace, true, stream);
+}
+
+int32_t ld_latent_decode(const ld_problem* p, const void* q_latent, const void* q_rope, const ld_kv_cache* cache,
+                         const int32_t* block_table, const int32_t* seq_lens, void* out, float* lse, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  const int32_t r = ld_plan_decode(p, q_latent, q_rope, cache, block_table, seq_lens, out, lse, workspace,
+                                   workspace_bytes, stream);
+  if (r != LD_OK || p->batch == 0) return r;
   return ld_combine_planned(p, out, lse, workspace, workspace_bytes, stream);
 }
 

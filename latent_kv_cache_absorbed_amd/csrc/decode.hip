@@ -99,149 +99,6 @@ struct Cfg {
 // ------------------------------------------------------------------------------------------
 // the decode kernel
 // ------------------------------------------------------------------------------------------
-// Fused plan.  Wave 0 of every work group applies the planner rule (plan_common.h) to seq_lens:
-// the unit count, then the unit this work group takes (same XCD-blocked mapping as with a stored
-// plan), then that unit's sequence, split and token range, which it leaves in u[0..4] (u[0] = -1:
-// no unit).  The plan arrays the combine reads are written on the way: each sequence's entries and
-// tasks by the first work group of its first unit, the unit record by the unit's first work group,
-// and the header, the entries of empty sequences (which have no unit) and the zeroed combine
-// arrival counters by work group 0.
-__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int t = __shfl_up(v, off);
-    if (lane >= off) v += t;
-  }
-  return v;
-}
-
-__device__ __forceinline__ void fused_plan_unit(const DecodeArgs& a, int x, int xcd, int yy, int sb, int* u) {
-  const PlanArgs& P = a.plan;
-  const int lane = threadIdx.x & 63;
-  // the lengths of the first 64 * kFusedLens sequences are read once, into registers
-  constexpr int kFusedLens = 4;
-  int len[kFusedLens];
-#pragma unroll
-  for (int k = 0; k < kFusedLens; ++k) {
-    const int bb = lane + 64 * k;
-    len[k] = (64 * k < P.batch && bb < P.batch) ? P.seq_lens[bb] : 0;
-  }
-  auto seq = [&](int chunk_, int base) {
-    const int bb = base + lane;
-    const int k = base >> 6;
-    int raw = 0;
-#pragma unroll
-    for (int j = 0; j < kFusedLens; ++j)
-      if (j == k) raw = len[j];
-    if (k >= kFusedLens && bb < P.batch) raw = P.seq_lens[bb];
-    return plan_seq_len(P, chunk_, bb, raw);
-  };
-  const int chunk = plan_auto_chunk(P, lane);
-  int tn = 0, tc = 0, tm = 0;
-  for (int base = 0; base < P.batch; base += 64) {
-    const SeqPlan sp = seq(chunk, base);
-    tn = min(tn + sp.n, 1 << 30);
-    tc = min(tc + sp.nc, 1 << 30);
-    tm += sp.mc;
-  }
-  for (int off = 32; off > 0; off >>= 1) {
-    tn = min(tn + __shfl_xor(tn, off), 1 << 30);
-    tc = min(tc + __shfl_xor(tc, off), 1 << 30);
-    tm += __shfl_xor(tm, off);
-  }
-  const int nunits = min(tn, P.max_units);
-  if (x == 0) {
-    if (lane == 0) {
-      P.header[0] = nunits;
-      P.header[1] = chunk;
-      P.header[2] = min(tc, P.max_tasks);
-      P.header[3] = min(tm, P.max_multi);
-    }
-    for (int i = lane; i < P.ccount_n; i += 64) P.ccount[i] = 0;  // combine arrival counters
-    // empty sequences: one combine task each, which writes zeros
-    int cn = 0, cc = 0;
-    for (int base = 0; base < P.batch; base += 64) {
-      const int b = base + lane;
-      const SeqPlan sp = seq(chunk, base);
-      const int in = wave_incl_scan(sp.n, lane), ic = wave_incl_scan(sp.nc, lane);
-      if (b < P.batch && sp.n == 0) {
-        const int ftask = cc + ic - sp.nc;
-        P.seqs[4 * b] = 0;
-        P.seqs[4 * b + 1] = cn + in;
-        P.seqs[4 * b + 2] = ftask;
-        P.seqs[4 * b + 3] = 1;
-        if (ftask < P.max_tasks) {
-          P.tasks[2 * ftask] = b;
-          P.tasks[2 * ftask + 1] = 0;
-        }
-      }
-      cn += __shfl(in, 63);
-      cc += __shfl(ic, 63);
-    }
-  }
-  const int per = (nunits + 7) >> 3;
-  const int unit = xcd * per + yy;
-  if (yy >= per || unit >= nunits) {
-    if (lane == 0) u[0] = -1;
-    return;
-  }
-  // the sequence holding the unit: first_b <= unit < first_b + n_b
-  int cn = 0, cc = 0, cm = 0;
-  int b = -1, first = 0, ftask = 0, mi = 0, L = 0, ck = 1, n = 0, nc = 0, mc = 0;
-  for (int base = 0; base < P.batch; base += 64) {
-    const SeqPlan sp = seq(chunk, base);
-    const int in = wave_incl_scan(sp.n, lane), ic = wave_incl_scan(sp.nc, lane), im = wave_incl_scan(sp.mc, lane);
-    const int f = cn + in - sp.n;
-    const unsigned long long hit = __ballot(base + lane < P.batch && unit >= f && unit < f + sp.n);
-    if (hit) {
-      const int src = __ffsll(hit) - 1;
-      b = base + src;
-      first = __shfl(f, src);
-      ftask = __shfl(cc + ic - sp.nc, src);
-      mi = __shfl(cm + im - sp.mc, src);
-      L = __shfl(sp.L, src);
-      ck = __shfl(sp.ck, src);
-      n = __shfl(sp.n, src);
-      nc = __shfl(sp.nc, src);
-      mc = __shfl(sp.mc, src);
-      break;
-    }
-    cn += __shfl(in, 63);
-    cc += __shfl(ic, 63);
-    cm += __shfl(im, 63);
-  }
-  if (b < 0) {  // unreachable: the units are counted from the same lengths
-    if (lane == 0) u[0] = -1;
-    return;
-  }
-  const int s = unit - first;
-  const int t_begin = s * ck;
-  const int t_end = min(L, (s + 1) * ck);
-  if (lane == 0) {
-    u[0] = unit;
-    u[1] = b;
-    u[2] = t_begin;
-    u[3] = t_end;
-    u[4] = n;
-  }
-  if (sb != 0) return;
-  if (lane == 0) P.units[unit] = Unit{b, t_begin, t_end, s};
-  if (s != 0) return;
-  if (lane == 0) {
-    P.seqs[4 * b] = n;
-    P.seqs[4 * b + 1] = first;
-    P.seqs[4 * b + 2] = ftask;
-    P.seqs[4 * b + 3] = nc;
-    if (mc && mi < P.max_multi) P.multi[mi] = b;
-  }
-  for (int c = lane; c < nc; c += 64) {
-    if (ftask + c < P.max_tasks) {
-      P.tasks[2 * (ftask + c)] = b;
-      P.tasks[2 * (ftask + c) + 1] = c;
-    }
-  }
-}
-
 // ------------------------------------------------------------------------------------------
 template <int KV, int DL, int DR, int KIND, int NSETS, int HB, int SPLIT>
 __global__ __launch_bounds__(NSETS* HB* SPLIT * 64) void decode_kernel(DecodeArgs a,
@@ -828,6 +685,7 @@ bool decode_instantiated(const ld_problem& p, int nsets, int hblocks) {
 }
 
 int launch_decode(const ld_problem& p, const DecodeArgs& a, void* stream) {
+  if (decode_pipe_serves(p, a.nsets, a.hblocks)) return launch_decode_pipe(p, a, stream);
   const int kv = kv_code(p), kind = kind_code(p), dl = p.d_latent, dr = p.d_rope;
 #define LD_RUN(KV_, DL_, DR_, KIND_, NS_, HB_, SP_)                                               \
   if (kv == KV_ && dl == DL_ && dr == DR_ && kind == KIND_ && a.nsets == NS_ && a.hblocks == HB_) \
@@ -852,6 +710,7 @@ int wgs_per_cu_of() {
 }
 
 int decode_wgs_per_cu(const ld_problem& p, int nsets, int hblocks) {
+  if (decode_pipe_serves(p, nsets, hblocks)) return decode_pipe_wgs_per_cu();
   const int kv = kv_code(p), kind = kind_code(p), dl = p.d_latent, dr = p.d_rope;
 #define LD_OCC(KV_, DL_, DR_, KIND_, NS_, HB_, SP_) \
   if (kv == KV_ && dl == DL_ && dr == DR_ && kind == KIND_ && nsets == NS_ && hblocks == HB_) \

@@ -6,6 +6,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "ld_internal.h"
 
 namespace ld {
@@ -46,8 +48,30 @@ __device__ __forceinline__ void wait_vmcnt() {
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // 16-byte global -> LDS copy per lane; the LDS destination of lane i is lds + 16 i.
-__device__ __forceinline__ void dma16(const void* gsrc, char* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds(gsrc, (__attribute__((address_space(3))) void*)(lds_wave_base), 16, 0, 0);
+__device__ __forceinline__ void dma16(const char* base, unsigned voff, char* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(base + voff, (__attribute__((address_space(3))) void*)(lds_wave_base), 16, 0, 0);
+}
+
+// The same copy written out (global_load_lds_dwordx4; M0 holds the wave's LDS address).  The
+// compiler models the builtin copy as a flat access that may also count in lgkmcnt, and then waits
+// for every LDS read in flight (lgkmcnt(0)) before each use of any of them, which exposes the LDS
+// latency of every MFMA operand; the written-out copy leaves its LDS-read waits exact.  The copy
+// counts in vmcnt only, and nothing of it is visible to the compiler: a kernel that uses it waits for
+// its copies itself (wait_vmcnt, then a barrier) before any wave reads the stage, and uses M0 for
+// nothing else.  lds_wave_base must be a direct pointer into a __shared__ array (so that its LDS
+// address folds to a constant plus an offset).
+__device__ __forceinline__ void dma16_asm(const char* base, unsigned voff, char* lds_wave_base) {
+  const unsigned lds = (unsigned)(uintptr_t)(__attribute__((address_space(3))) char*)(lds_wave_base);
+  const unsigned long long b = (unsigned long long)(uintptr_t)base;
+  const unsigned long long bs = ((unsigned long long)__builtin_amdgcn_readfirstlane((unsigned)(b >> 32)) << 32) |
+                                (unsigned)__builtin_amdgcn_readfirstlane((unsigned)b);
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"  // M0 is reserved; the kernels using this copy use it for nothing else
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %2"
+               :
+               : "v"(voff), "s"(__builtin_amdgcn_readfirstlane(lds)), "s"(bs)
+               : "memory", "m0");
+#pragma clang diagnostic pop
 }
 
 // ------------------------------------------------------------------------------------------
@@ -145,9 +169,9 @@ __device__ __forceinline__ uint4 e4m3x8_to_bf16x8(unsigned lo, unsigned hi) {
 // unit's end repeat its last row), and logical LDS row byte b comes from byte col(b) of it.  The
 // address is formed as a wave-uniform 64-bit base plus a 32-bit per-lane offset, which the copy
 // instruction takes as an SGPR pair and one VGPR.
-template <int RB, int MSK, int NW, int FIRST, class ColFn>
+template <int RB, int MSK, int NW, int FIRST, class ColFn, bool ASM = false>
 __device__ __forceinline__ void dma_region(char* region, int wave, int lane, const char* rows, int row_bytes, int tlast,
-                                           ColFn col) {
+                                           ColFn col, std::integral_constant<bool, ASM> = {}) {
   constexpr int blocks = kTile * RB / 1024;
   constexpr int iters = (blocks + NW - 1) / NW;
   constexpr int shift = FIRST % NW;
@@ -164,7 +188,10 @@ __device__ __forceinline__ void dma_region(char* region, int wave, int lane, con
       const int tu = min(t_first, tlast);
       unsigned voff = (unsigned)((min(t, tlast) - tu) * row_bytes + col(c << 4));
       asm volatile("" : "+v"(voff));  // computed here, not hoisted as a 64-bit address per block
-      dma16(rows + (size_t)tu * row_bytes + voff, region + q * 1024);
+      if constexpr (ASM)
+        dma16_asm(rows + (size_t)tu * row_bytes, voff, region + q * 1024);
+      else
+        dma16(rows + (size_t)tu * row_bytes, voff, region + q * 1024);
     }
   }
 }

@@ -1,0 +1,490 @@
+// Software-pipelined decode kernel for the latent shapes whose whole query set fits one work group
+// of one wave per 32-head block (absorbed MLA: 128 heads over one 576-dim shared row), gfx950.
+// See include/latent_decode.h for the operation and its sources.
+//
+// One wave per SIMD, each wave one block of 32 heads over all score and value dims:
+//   Q (32 heads x 576 bf16)  144 VGPRs, loaded once per unit
+//   O (32 heads x 512 f32)   256 AGPRs, accumulated by the P.V MFMAs
+//   S (32 tokens x 32 heads)  16 VGPRs per stage, two stages live
+// No wave shares scores with another, so the only work-group barrier is the one that recycles the
+// stage buffers.  Each wave runs its stages as a software pipeline: while the score MFMAs of stage
+// n+1 run, the wave computes the softmax of stage n between them, then issues the P.V MFMAs of stage
+// n.  The MFMA pipe of the SIMD so stays busy with one wave, and the softmax costs no MFMA time.
+//
+// Softmax reference.  O lives in AGPRs, which VALU instructions cannot scale in place, so the kernel
+// never rescales O: every head takes the max of its unit's first stage as a fixed reference r (log2
+// domain) and accumulates p = 2^(s - r).  Probabilities above 1 are fine up to 2^kRefSlack; a stage
+// whose max exceeds r + kRefSlack flags the unit, and the work group then runs the unit once more
+// with r = the unit's exact max (known from the first pass), where no p exceeds 1.  The normalised
+// result does not depend on r (it cancels between numerator and denominator).
+//
+// Stage buffers, DMA, swizzle, MFMA layouts and the split-partial format are those of decode.hip
+// (decode_common.h), so the plan and the combine are shared.
+#include <hip/hip_runtime.h>
+
+#include "decode_common.h"
+#include "plan_common.h"
+#include "ld_internal.h"
+
+namespace ld {
+namespace {
+
+// p = 2^(s - r) may reach 2^kRefSlack before the unit is run again with the exact max: far below
+// the fp32 / bf16 range, so sums of up to 2^20 stages x 32 tokens of such values stay finite.
+constexpr float kRefSlack = 64.f;
+
+template <int DL, int DR, int HB>
+struct PCfg {
+  using M = Mma<KV_BF16>;
+  static constexpr int WAVES = HB;
+  static constexpr int THREADS = WAVES * kWaveSize;
+  static constexpr int KL = DL / 16;                 // latent k-steps of S
+  static constexpr int KR = DR / 16;                 // rope k-steps of S
+  static constexpr int KS = KL + KR;
+  static constexpr int CB = DL / 32;                 // 32-column blocks of O
+  static constexpr int LW = DL * 2;                  // latent row bytes in LDS
+  static constexpr int RW = DR * 2;                  // rope row bytes in LDS
+  static constexpr int SETCH = DL * 2 / 16;
+  static constexpr int MLS = cmin(SETCH - 1, swz_mask(LW));
+  static constexpr int MR = swz_mask(RW);
+  static constexpr int ROPE_OFF = kTile * LW;
+  static constexpr int BUF = ROPE_OFF + kTile * RW;
+  static constexpr int NBUF = 4;
+  static constexpr int DMA_BLOCKS = kTile * (LW + RW) / 1024;
+  static constexpr int DMA_PER_WAVE = DMA_BLOCKS / WAVES;
+  static constexpr int NKL = (MLS + 1) / 2;          // latent k-steps per swizzle group
+  static constexpr int NVT = (MLS >> 2) + 1;          // V column blocks per swizzle group
+  static_assert(DMA_BLOCKS % WAVES == 0, "every wave issues the same number of copies");
+  static_assert(KS % 4 == 0 && CB % 4 == 0, "k-steps and column blocks come in groups of four");
+  static_assert(2 * KR <= MR + 1, "rope row must lie in one swizzle group");
+  static_assert(pow2(LW) && pow2(RW) && (kTile * RW) % 1024 == 0, "row sizes");
+  static_assert(NBUF * BUF + 4 * kUnitPages + 64 <= 160 * 1024, "LDS budget");
+};
+
+// P.V MFMA accumulating into AGPRs.  The score MFMAs of this kernel are compiler builtins with their
+// results in VGPRs (the softmax reads them), and one function holds one MFMA register form, so the
+// P.V MFMAs, whose 256 accumulators fill the AGPRs, are written out.
+__device__ __forceinline__ void mfma_pv(floatx16& acc, bf16x8_t a, bf16x8_t b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+// Wait states after the last P.V MFMA before its accumulators are read or rewritten.
+__device__ __forceinline__ void mfma_pv_drain() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); }
+
+template <int DL, int DR, int HB>
+__global__ __launch_bounds__(HB * 64) void decode_pipe_kernel(DecodeArgs a, const int32_t* __restrict__ block_table) {
+  using C = PCfg<DL, DR, HB>;
+  using M = typename C::M;
+  __shared__ __attribute__((aligned(128))) char lds_b0[C::BUF];
+  __shared__ __attribute__((aligned(128))) char lds_b1[C::BUF];
+  __shared__ __attribute__((aligned(128))) char lds_b2[C::BUF];
+  __shared__ __attribute__((aligned(128))) char lds_b3[C::BUF];
+  __shared__ int lds_pages[kUnitPages];
+  __shared__ int s_unit[5];
+  __shared__ int s_again;
+
+  // unit of this work group: the same XCD-blocked mapping as decode_kernel
+  const int x = blockIdx.x;
+  const int xcd = x & 7;
+  const int y = x >> 3;
+  const int sb = y % a.wg_per_unit;
+  const int yy = y / a.wg_per_unit;
+  int unit, b, t_begin, t_end, nsplit;
+  if (a.fused_plan) {
+    if (threadIdx.x < 64) fused_plan_unit(a, x, xcd, yy, sb, s_unit);
+    __syncthreads();
+    if (s_unit[0] < 0) return;
+    unit = s_unit[0];
+    b = s_unit[1];
+    t_begin = s_unit[2];
+    t_end = s_unit[3];
+    nsplit = s_unit[4];
+  } else {
+    const int nunits = a.header[0];
+    const int per = (nunits + 7) >> 3;
+    if (yy >= per) return;
+    unit = xcd * per + yy;
+    if (unit >= nunits) return;
+    const Unit u = a.units[unit];
+    b = u.b;
+    t_begin = u.t_begin;
+    t_end = u.t_end;
+    nsplit = a.seqs[4 * b];
+  }
+  // query token qi of the unit's work groups (several query tokens: token qi sees the first
+  // L_b - qlen + 1 + qi rows); one set (the whole head set of the latent row)
+  const int qi = sb;
+  const int gs = qi * a.cache_groups;
+  if (a.qlen > 1) {
+    const int Lb = clampi(a.seq_lens[b], 0, a.max_pages * a.page_size);
+    t_end = max(t_begin, min(t_end, Lb - a.qlen + 1 + qi));
+  }
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int h = lane >> 5;
+  const int col = lane & 31;
+  const int hb = wave;
+  const int head_in_set = hb * 32 + col;
+  const bool valid = head_in_set < a.heads_per_set;
+  const int head = gs * a.heads_per_set + (valid ? head_in_set : 0);
+  const int32_t* __restrict__ bt_row = block_table + (size_t)b * a.max_pages;
+  const int page_size = a.page_size;
+  const int first_page = t_begin / page_size;
+  const int unit_pages = t_end > t_begin ? (t_end - 1) / page_size - first_page + 1 : 0;
+  for (int i = threadIdx.x; i < unit_pages && i < kUnitPages; i += C::THREADS)
+    lds_pages[i] = clampi(bt_row[first_page + i], 0, a.num_pages - 1);
+  __syncthreads();
+
+  const int grow_bytes = DL * 2 + DR * 2;
+  const char* kbase = static_cast<const char*>(a.k);
+  // Stage copies.  Wave w copies 1 KB blocks w, w + 4, .., w + 28 of the latent region and block w of
+  // the rope region (the dealing of dma_region): copy j < 8 is latent block w + 4 j, copy 8 the rope
+  // block.  The stage's rows come from one page: its id is read from LDS once per stage.
+  struct StageSrc {
+    const char* rows;
+    int tlast;
+  };
+  auto stage_src = [&](int stage0) -> StageSrc {
+    const int pi = stage0 / page_size - first_page;
+    const int page = __builtin_amdgcn_readfirstlane(lds_pages[min(pi, kUnitPages - 1)]);
+    const size_t r0 = (size_t)page * page_size + (stage0 % page_size);
+    return StageSrc{kbase + r0 * (size_t)grow_bytes, t_end - 1 - stage0};
+  };
+  auto copy_block = [&](const StageSrc& src, char* buf, int j) __attribute__((always_inline)) {
+    // the per-lane offsets are derived from the lane index afresh (the empty asm hides that they are
+    // loop invariant), so they do not hold registers across the loop
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    if (j < 8) {
+      const int q = wave + C::WAVES * j;
+      constexpr int CPR = C::LW / 16;
+      const int t = (q * 1024) / C::LW + ln / CPR;
+      const int cp = ln % CPR;
+      const int c = (cp & ~C::MLS) | ((cp & C::MLS) ^ (swz_key(t) & C::MLS));
+      const int tf = (q * 1024) / C::LW;
+      const int tu = min(tf, src.tlast);
+      unsigned voff = (unsigned)((min(t, src.tlast) - tu) * grow_bytes + (c << 4));
+      asm volatile("" : "+v"(voff));
+      dma16_asm(src.rows + (size_t)tu * grow_bytes, voff, buf + q * 1024);
+    } else {
+      const int q = wave;
+      constexpr int CPR = C::RW / 16;
+      const int t = (q * 1024) / C::RW + ln / CPR;
+      const int cp = ln % CPR;
+      const int c = (cp & ~C::MR) | ((cp & C::MR) ^ (swz_key(t) & C::MR));
+      const int tf = (q * 1024) / C::RW;
+      const int tu = min(tf, src.tlast);
+      unsigned voff = (unsigned)((min(t, src.tlast) - tu) * grow_bytes + DL * 2 + (c << 4));
+      asm volatile("" : "+v"(voff));
+      dma16_asm(src.rows + (size_t)tu * grow_bytes, voff, buf + C::ROPE_OFF + q * 1024);
+    }
+  };
+  auto issue_stage = [&](int stage0, char* buf) {
+    const StageSrc src = stage_src(stage0);
+#pragma unroll
+    for (int j = 0; j < C::DMA_PER_WAVE; ++j) copy_block(src, buf, j);
+  };
+  static_assert(C::DMA_PER_WAVE == 9 && C::DMA_BLOCKS == 36 && C::LW == 1024, "copy dealing of the 576-dim row");
+
+  // this lane's query fragments (B operand of S^T = K . Q^T): all latent and rope k-steps
+  bf16x8_t qf[C::KS];
+  {
+    const size_t qrow = (size_t)b * a.heads + head;
+    const __bf16* qlp = static_cast<const __bf16*>(a.q_lat) + qrow * DL + h * 8;
+    const __bf16* qrp = static_cast<const __bf16*>(a.q_rope) + qrow * DR + h * 8;
+#pragma unroll
+    for (int k = 0; k < C::KL; ++k) {
+      uint4 v = *reinterpret_cast<const uint4*>(qlp + k * 16);
+      if (!valid) v = make_uint4(0u, 0u, 0u, 0u);
+      qf[k] = __builtin_bit_cast(bf16x8_t, v);
+    }
+#pragma unroll
+    for (int j = 0; j < C::KR; ++j) {
+      uint4 v = *reinterpret_cast<const uint4*>(qrp + j * 16);
+      if (!valid) v = make_uint4(0u, 0u, 0u, 0u);
+      qf[C::KL + j] = __builtin_bit_cast(bf16x8_t, v);
+    }
+  }
+
+  // per-lane LDS offsets (see decode.hip): S operand of k-step k is klat0 ^ 32 (k % NKL) (+ group
+  // offset); rope k-step j is krope0 ^ 32 j; V^T operand of column block c is vtr0[rb] ^ 64 (c % NVT)
+  const int tr = M::row_token(col);
+  const int klat0 = lds_off(tr, C::LW, C::MLS, h * 16);
+  const int krope0 = lds_off(tr, C::RW, C::MR, h * 16);
+  int vtr0[2];
+  {
+    const int g16 = lane >> 4;
+    const int L16 = lane & 15;
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      const int tt = 8 * (g16 >> 1) + 4 * rb + (L16 >> 2);
+      vtr0[rb] = lds_off(tt, C::LW, C::MLS, 2 * (g16 & 1) * 16 + (L16 & 3) * 8);
+    }
+  }
+  auto s_operand = [&](const char* cur, int k, int kl, int kr) -> bf16x8_t {
+    if (k < C::KL) {
+      const int o = (kl ^ (32 * (k & (C::NKL - 1)))) + 32 * (k & ~(C::NKL - 1));
+      return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(cur + o));
+    }
+    return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(cur + C::ROPE_OFF + (kr ^ (32 * (k - C::KL)))));
+  };
+
+  const int nstage = (t_end - t_begin + kTile - 1) / kTile;
+  const float c2 = a.scale_log2;
+
+  floatx16 acc[C::CB];
+  float l_run = 0.f;     // sum of 2^(score - ref) over the unit
+  float ref = 0.f;       // fixed reference of this head (log2 domain)
+  float mmax = -INFINITY;  // exact max of this head's scaled scores over the unit (log2 domain)
+  bool over = false;     // a stage max exceeded ref + kRefSlack
+  bool fixed = false;    // second pass: ref = mmax of the first
+
+  // The score MFMAs of one stage (36), with the softmax work `work(g)` of the previous stage placed
+  // after each group g of four; operands are read two k-steps ahead.
+  auto scores = [&](const char* cur, floatx16& S, auto&& work) __attribute__((always_inline)) {
+    int kl = klat0, kr = krope0;
+    asm volatile("" : "+v"(kl), "+v"(kr));
+    bf16x8_t ring[4];
+    ring[0] = s_operand(cur, 0, kl, kr);
+    ring[1] = s_operand(cur, 1, kl, kr);
+#pragma unroll
+    for (int g = 0; g < C::KS / 4; ++g) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int k = 4 * g + j;
+        if (k + 2 < C::KS) ring[(k + 2) & 3] = s_operand(cur, k + 2, kl, kr);
+        S = M::mma(ring[k & 3], qf[k], k == 0 ? floatx16{} : S);
+      }
+      work(g);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // softmax of one stage's scores, in C::KS / 4 pieces (g = 0 .. KS/4 - 1); the state it leaves:
+  // pf (P^T fragments, bf16), and l_run / ref / mmax / over updated
+  bf16x8_t pf[2];
+  float sv[16], mt = 0.f;
+  auto softmax_piece = [&](const floatx16& S, int g, bool first, bool last_stage, int stage0)
+                           __attribute__((always_inline)) {
+    constexpr int G = C::KS / 4;
+    if (g == 0) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sv[i] = S[i];
+      if (last_stage) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sv[i] = (stage0 + M::token_of(i, h) < t_end) ? sv[i] : -INFINITY;
+      }
+      mt = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])), fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
+      mt = fmaxf(mt, fmaxf(fmaxf(fmaxf(sv[8], sv[9]), fmaxf(sv[10], sv[11])),
+                           fmaxf(fmaxf(sv[12], sv[13]), fmaxf(sv[14], sv[15]))));
+    } else if (g == 1) {
+      mt = fmaxf(mt, xor32(mt)) * c2;
+      if (!fixed && first) ref = mt;
+      mmax = fmaxf(mmax, mt);
+      over |= mt > ref + kRefSlack;
+    } else if (g >= 2 && g < 6) {
+#pragma unroll
+      for (int i = 4 * (g - 2); i < 4 * (g - 1); ++i) sv[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[i], c2, -ref));
+    } else if (g == 6) {
+      bf16x8_t f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) f[j] = (__bf16)sv[j];
+      pf[0] = f;
+    } else if (g == 7) {
+      bf16x8_t f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) f[j] = (__bf16)sv[8 + j];
+      pf[1] = f;
+    } else if (g == G - 1) {
+      typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+      const bf16x2_t one2 = {(__bf16)1.f, (__bf16)1.f};
+      float psum = 0.f;
+#pragma unroll
+      for (int p2 = 0; p2 < 2; ++p2)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          psum = __builtin_amdgcn_fdot2_f32_bf16(bf16x2_t{pf[p2][2 * j], pf[p2][2 * j + 1]}, one2, psum, false);
+      l_run += psum + xor32(psum);
+    }
+  };
+  static_assert(C::KS / 4 == 9, "the softmax is laid out in nine pieces");
+
+  // O^T += V^T . P^T over all column blocks, in groups of four MFMAs (`work(g)` after group g); the
+  // V operands are read two MFMAs ahead
+  auto pv = [&](const char* cur, auto&& work) __attribute__((always_inline)) {
+    int v0 = vtr0[0], v1 = vtr0[1];
+    asm volatile("" : "+v"(v0), "+v"(v1));
+    auto vop = [&](int i) -> bf16x8_t {
+      const int p2 = i / C::CB, c = i % C::CB;
+      const int cstat = 16 * p2 * C::LW + 64 * (c & ~(C::NVT - 1));
+      const int cx = 64 * (c & (C::NVT - 1));
+      const bf16x4_t lo = lds_read_tr(cur + (v0 ^ cx) + cstat);
+      const bf16x4_t hi = lds_read_tr(cur + (v1 ^ cx) + cstat);
+      return bf16x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    };
+    constexpr int N = 2 * C::CB;
+    bf16x8_t ring[4];
+    ring[0] = vop(0);
+    ring[1] = vop(1);
+#pragma unroll
+    for (int g = 0; g < N / 4; ++g) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int i = 4 * g + j;
+        if (i + 2 < N) ring[(i + 2) & 3] = vop(i + 2);
+        mfma_pv(acc[i % C::CB], ring[i & 3], pf[i / C::CB]);
+      }
+      work(g);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // this wave's copies of stage n have landed (those of the later stage already issued may not)
+  auto wait_stage = [&](int n) __attribute__((always_inline)) {
+    if (n + 1 < nstage)
+      wait_vmcnt<C::DMA_PER_WAVE>();
+    else
+      wait_vmcnt<0>();
+  };
+
+  for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+    for (int k = 0; k < C::CB; ++k) acc[k] = floatx16{};
+    l_run = 0.f;
+    over = false;
+    if (pass == 1) {
+      ref = mmax;
+      fixed = true;
+    }
+    if (nstage > 0) {
+      // prologue: stages 0..2 in flight, scores of stage 0
+      issue_stage(t_begin, lds_b0);
+      if (nstage > 1) issue_stage(t_begin + kTile, lds_b1);
+      if (nstage > 2) issue_stage(t_begin + 2 * kTile, lds_b2);
+      if (nstage >= 3)
+        wait_vmcnt<2 * C::DMA_PER_WAVE>();
+      else if (nstage == 2)
+        wait_vmcnt<C::DMA_PER_WAVE>();
+      else
+        wait_vmcnt<0>();
+      lds_barrier();
+      floatx16 SA, SB;
+      scores(lds_b0, SA, [](int) {});
+      // iteration n: scores of stage n+1 with the softmax of stage n between them, then P.V of n
+      auto iter = [&](int n, floatx16& S, floatx16& Snext, char* cur, char* nxt, char* refill)
+                      __attribute__((always_inline)) {
+        const int stage0 = t_begin + n * kTile;
+        const bool refill_now = n + 3 < nstage;
+        const StageSrc src = stage_src(t_begin + (n + 3) * kTile);
+        if (n + 1 < nstage) {
+          wait_stage(n + 1);
+          lds_barrier();
+          // the nine copies of stage n + 3 are spread over the iteration, one per two groups of MFMAs
+          // (five among the score MFMAs, four among the P.V MFMAs): a copy instruction holds up the
+          // wave that issues it, so they are paced rather than issued in a burst
+          scores(nxt, Snext, [&](int g) {
+            softmax_piece(S, g, n == 0, false, stage0);
+            if (refill_now && (g & 1) == 0) copy_block(src, refill, g / 2);
+          });
+        } else {
+#pragma unroll
+          for (int g = 0; g < C::KS / 4; ++g) softmax_piece(S, g, n == 0, true, stage0);
+        }
+        pv(cur, [&](int g) __attribute__((always_inline)) {
+          if (refill_now && (g & 1)) copy_block(src, refill, 5 + g / 2);
+        });
+      };
+      for (int n0 = 0; n0 < nstage; n0 += 4) {
+        iter(n0, SA, SB, lds_b0, lds_b1, lds_b3);
+        if (n0 + 1 < nstage) iter(n0 + 1, SB, SA, lds_b1, lds_b2, lds_b0);
+        if (n0 + 2 < nstage) iter(n0 + 2, SA, SB, lds_b2, lds_b3, lds_b1);
+        if (n0 + 3 < nstage) iter(n0 + 3, SB, SA, lds_b3, lds_b0, lds_b2);
+      }
+    }
+    mfma_pv_drain();
+    // run the unit again with the exact max if any head of the work group overflowed its reference
+    if (threadIdx.x == 0) s_again = 0;
+    __syncthreads();
+    if (__any(over) && lane == 0) s_again = 1;
+    __syncthreads();
+    if (!s_again || pass == 1) break;
+    __syncthreads();
+  }
+
+  // ---- epilogue (the layouts of decode.hip with one wave per head block)
+  const float inv_l = l_run > 0.f ? 1.f / l_run : 0.f;
+  const float lse_v = (ref + log2f(l_run)) * kLn2;
+  if (nsplit == 1) {
+    if (!valid) return;
+    const size_t orow = (size_t)b * a.rows + gs * a.heads_per_set + head_in_set;
+    if (h == 0) a.lse[orow] = lse_v;
+#pragma unroll
+    for (int k = 0; k < C::CB; ++k) {
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int c = k * 32 + 8 * g4 + 4 * h;
+        const float o0 = acc[k][4 * g4 + 0] * inv_l, o1 = acc[k][4 * g4 + 1] * inv_l;
+        const float o2 = acc[k][4 * g4 + 2] * inv_l, o3 = acc[k][4 * g4 + 3] * inv_l;
+        if (a.out_bf16) {
+          __bf16* dst = static_cast<__bf16*>(a.out) + orow * DL + c;
+          *reinterpret_cast<bf16x4_t*>(dst) = bf16x4_t{(__bf16)o0, (__bf16)o1, (__bf16)o2, (__bf16)o3};
+        } else {
+          float* dst = static_cast<float*>(a.out) + orow * DL + c;
+          *reinterpret_cast<float4*>(dst) = make_float4(o0, o1, o2, o3);
+        }
+      }
+    }
+  } else {
+    const size_t blk = ((size_t)unit * a.groups + gs) * HB + hb;
+    if (h == 0) a.part_lse[blk * 32 + col] = lse_v;
+    if (a.part_bf16) {
+      __bf16* dst = static_cast<__bf16*>(a.part_out) + blk * (32 * DL);
+#pragma unroll
+      for (int k = 0; k < C::CB; ++k)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          bf16x8_t v;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] = (__bf16)(acc[k][8 * j + e] * inv_l);
+          *reinterpret_cast<bf16x8_t*>(dst + ((k * 2 + j) * 64 + lane) * 8) = v;
+        }
+    } else {
+      float* dst = static_cast<float*>(a.part_out) + blk * (32 * DL);
+#pragma unroll
+      for (int k = 0; k < C::CB; ++k)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          *reinterpret_cast<float4*>(dst + ((k * 4 + j) * 64 + lane) * 4) =
+              make_float4(acc[k][4 * j] * inv_l, acc[k][4 * j + 1] * inv_l, acc[k][4 * j + 2] * inv_l,
+                          acc[k][4 * j + 3] * inv_l);
+    }
+  }
+}
+
+}  // namespace
+
+// The pipelined kernel serves bf16 latent caches with one set of 128 heads (absorbed MLA) and one
+// query token per work group: returns hipError_t, or -1 when the shape is not its own.
+int launch_decode_pipe(const ld_problem& p, const DecodeArgs& a, void* stream) {
+  if (!decode_pipe_serves(p, a.nsets, a.hblocks)) return -1;
+  const int units8 = (a.max_units + 7) / 8 * 8;
+  hipLaunchKernelGGL((decode_pipe_kernel<512, 64, 4>), dim3(units8 * a.wg_per_unit), dim3(4 * kWaveSize), 0,
+                     static_cast<hipStream_t>(stream), a, a.block_table);
+  return (int)hipGetLastError();
+}
+
+bool decode_pipe_serves(const ld_problem& p, int nsets, int hblocks) {
+  return p.kv_dtype == LD_BF16 && p.q_dtype == LD_BF16 && p.variant == LD_VARIANT_MLA && p.d_latent == 512 &&
+         p.d_rope == 64 && nsets == 1 && hblocks == 4;
+}
+
+int decode_pipe_wgs_per_cu() {
+  static const int n = [] {
+    int v = 0;
+    const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+        &v, reinterpret_cast<const void*>(decode_pipe_kernel<512, 64, 4>), 4 * kWaveSize, 0);
+    return (e == hipSuccess && v > 0) ? v : 1;
+  }();
+  return n;
+}
+
+}  // namespace ld

@@ -164,6 +164,12 @@ struct ProjArgs {
   int32_t m, heads, n, k;
 };
 int launch_head_projection(const ProjArgs& a, int out_bf16, void* stream);
+// The software-pipelined kernel (decode_pipe.hip) for bf16 absorbed MLA with 128 heads per work group:
+// whether it serves the shape, its launcher (hipError_t, or -1 when it does not serve the shape) and
+// how many of its work groups fit on one CU.
+bool decode_pipe_serves(const ld_problem& p, int nsets, int hblocks);
+int launch_decode_pipe(const ld_problem& p, const DecodeArgs& a, void* stream);
+int decode_pipe_wgs_per_cu();
 // Whether a decode kernel is built for p's dtype/dims/kind with `nsets` sets per work group and
 // `hblocks` 32-head blocks per set.
 bool decode_instantiated(const ld_problem& p, int nsets, int hblocks);

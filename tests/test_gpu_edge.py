@@ -146,3 +146,23 @@ def test_split_combine_standalone_nan_lse():
         else:
             assert np.max(np.abs(o[i] - eo)) <= 1e-5 * max(1.0, np.max(np.abs(eo)))
             assert abs(l[i] - el) <= 1e-5 * max(1.0, abs(el))
+
+
+@pytest.mark.parametrize("splits,spikes", [(0, [64 * 5 + 40, 2999]), (1, [2000]), (3, [1100, 1101])])
+def test_score_far_above_the_first_rows(splits, spikes):
+    """Keys whose scores exceed every other row's by a factor above 2^400 in the softmax (a unit's later rows dominating
+    its first): the result is the oracle's, i.e. the weight concentrates on those keys, whatever reference
+    the kernel's softmax starts from (the absorbed-MLA kernel runs such a unit again with its exact max)."""
+    lens = [3000, 700]
+    inp = synth.make_inputs("mla", 2, 128, 1, 512, 64, lens, scale=1 / math.sqrt(192), seed=54)
+    q = inp.q_lat[0].float()                                  # [H, 512]
+    for t in spikes:
+        page, slot = int(inp.layout.block_table[0, t // 64]), t % 64
+        inp.k_pool[page, slot, :512] = (8.0 * q[0]).to(inp.k_pool.dtype)   # head 0 scores ~300 there
+    print(f"case score spikes at {spikes} splits={splits}", flush=True)
+    got_o, got_l = run_gpu(inp, num_splits=splits)
+    ref_o, ref_l = run_oracle(inp)
+    eo, el = row_rel_err(got_o, ref_o), lse_err(got_l, ref_l)
+    print(f"   out err {eo:.3e}  lse err {el:.3e}  head-0 lse {ref_l[0, 0]:.1f}", flush=True)
+    assert ref_l[0, 0] > 200                                   # the spike dominates head 0 by far
+    assert eo <= tolerance(inp) and el <= tolerance(inp)

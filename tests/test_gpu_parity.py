@@ -365,3 +365,24 @@ def test_graph_replay_matches_eager(lens):
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(d.out, out0) and torch.equal(d.lse, lse0), f"replay {r} differs from the eager run"
+
+
+def test_plan_decode_then_combine_is_the_step():
+    """ld_plan_decode followed by ld_combine_planned gives ld_latent_decode's bits (the benchmark times the
+    decode kernel inside the step this way)."""
+    import latent_kv_cache_absorbed_amd as lkd
+    from gpu_util import to_dev
+    for lens in ([40000] + [300 + 97 * i for i in range(9)], [5000, 64, 2600]):
+        inp = synth.make_inputs("mla", len(lens), 128, 1, 512, 64, lens, scale=_S, seed=33)
+        bt = torch.from_numpy(inp.layout.block_table).cuda()
+        sl = torch.from_numpy(inp.layout.seq_lens).cuda()
+        mk = lambda: lkd.Decoder(to_dev(inp.q_lat), to_dev(inp.q_rope), to_dev(inp.k_pool), bt, sl,  # noqa: E731
+                                 variant="mla", scale=inp.scale)
+        one, two = mk(), mk()
+        two.out.fill_(float("nan"))
+        two.workspace.fill_(0xFF)
+        one.run()
+        two.plan_decode()
+        two.combine()
+        torch.cuda.synchronize()
+        assert torch.equal(one.out, two.out) and torch.equal(one.lse, two.lse)
