@@ -44,6 +44,7 @@ PROFILES = os.path.join(ROOT, "profiles")
 DEFAULT_WORKLOAD = "mla_b64_l4k"
 LONG_WORKLOADS = ("mla_b1_l1m", "mlra4_b1_l1m", "gla2_fp8_b64_mixed")
 FLUSH_BYTES = 1 << 30
+XCDS = 8                        # MI355X: 8 XCDs of 32 CUs
 
 
 def flops_per_token_head(w) -> int:
@@ -258,7 +259,8 @@ def measure(name, steps, warmup, min_warmup_ms, dev, flush, num_splits=0, stages
         "tokens_per_s": round(inp.batch * inp.q_len / t_med, 1),
         "kv_tokens_per_s": round(float(lens.sum()) / t_med, 1),
         "hbm_frac_step": round((kv_bytes + q_bytes + out_bytes) / t_med / 1e9 / HBM_PEAK_GBS, 4),
-        "roofline": {"kernel": "decode_kernel", "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+        "roofline": {"kernel": "decode_pipe_kernel" if (w.variant == "mla" and inp.kv_dtype == "bf16" and inp.heads == 128)
+                     else "decode_kernel", "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": None if prof is None else prof.get("hbm_bytes_per_launch"),
                      "traffic_source": None if prof is None else os.path.relpath(traffic_path(name), ROOT),
@@ -364,6 +366,11 @@ def _counter(dir_: str, name: str):
     return out
 
 
+def is_decode(kernel_name: str) -> bool:
+    """The decode kernels (decode_kernel of decode.hip, decode_pipe_kernel of decode_pipe.hip)."""
+    return "decode_kernel" in kernel_name or "decode_pipe_kernel" in kernel_name
+
+
 def summarize_profile(workload: str, trace_dir: str, fetch_dir: str, write_dir: str, mfma_dir: str, copy_mib: int,
                       steps: int, commands: list[str], num_cus: int = 256) -> None:
     """Write profiles/decode_kernel_<workload>.md and profiles/decode_<workload>_traffic.json.
@@ -376,12 +383,12 @@ def summarize_profile(workload: str, trace_dir: str, fetch_dir: str, write_dir: 
     per = {}
     for r in rows:
         per.setdefault(r["Kernel_Name"], []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
-    dec_name = [k for k in per if "decode_kernel" in k][0]
+    dec_name = [k for k in per if is_decode(k)][0]
     in_step = per[dec_name][-2 * steps:]
     comb = {k: v for k, v in per.items() if "combine" in k}
     fetch, write = _counter(fetch_dir, "FETCH_SIZE"), _counter(write_dir, "WRITE_SIZE")
     copy_kib = copy_mib * 1024
-    pick = lambda d: [v for k, vs in d.items() if "decode_kernel" in k for v in vs]  # noqa: E731
+    pick = lambda d: [v for k, vs in d.items() if is_decode(k) for v in vs]  # noqa: E731
     # calibration: the copy of exactly copy_mib MiB reads and writes copy_kib KiB
     fcopy = [v for k, vs in fetch.items() if "copyBuffer" in k for v in vs if abs(v - copy_kib) < 0.6 * copy_kib]
     wcopy = [v for k, vs in write.items() if "copyBuffer" in k for v in vs if abs(v - copy_kib) < 0.6 * copy_kib]
@@ -392,9 +399,11 @@ def summarize_profile(workload: str, trace_dir: str, fetch_dir: str, write_dir: 
     hbm = (f_kib * fscale + w_kib * wscale) * 1024
     mf = {c: float(np.median(pick(_counter(mfma_dir, c))[-2 * steps:]))
           for c in ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CYCLES", "GRBM_GUI_ACTIVE", "SQ_INSTS_VALU_MFMA_MOPS_BF16")}
-    # SQ_VALU_MFMA_BUSY_CYCLES sums busy cycles over every SIMD (4 per CU); GRBM_GUI_ACTIVE counts the
-    # kernel's GPU-busy cycles once
-    mfma_busy = mf["SQ_VALU_MFMA_BUSY_CYCLES"] / (mf["GRBM_GUI_ACTIVE"] * num_cus * 4)
+    # SQ_VALU_MFMA_BUSY_CYCLES sums the MFMA-busy cycles of every SIMD (4 per CU): each 32x32x16 MFMA adds
+    # its 32 cycles, so it equals the MFMA count x 32.  GRBM_GUI_ACTIVE comes back summed over the
+    # XCDs (one GRBM each), so the kernel's own busy cycles are GRBM_GUI_ACTIVE / XCDS.
+    gpu_cycles = mf["GRBM_GUI_ACTIVE"] / XCDS
+    mfma_busy = mf["SQ_VALU_MFMA_BUSY_CYCLES"] / (gpu_cycles * num_cus * 4)
     t = {"workload": workload, "decode_source_sha": source_sha(), "hbm_bytes_per_launch": int(hbm),
          "fetch_kib_per_dispatch": f_kib, "write_kib_per_dispatch": w_kib, "fetch_scale": round(fscale, 5),
          "write_scale": round(wscale, 5), "calibration": f"plain device copy of {copy_mib} MiB",
@@ -429,7 +438,9 @@ def summarize_profile(workload: str, trace_dir: str, fetch_dir: str, write_dir: 
     lines += [f"- {c} {v:.4g}" for c, v in mf.items()]
     lines += [f"- MFMA bf16 flops counted (SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512): "
               f"{mf['SQ_INSTS_VALU_MFMA_MOPS_BF16'] * 512 / 1e9:.2f} GFLOP per launch"]
-    lines += [f"- MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x {num_cus} CUs x 4 SIMDs) = {mfma_busy:.4f}",
+    lines += [f"- kernel busy cycles = GRBM_GUI_ACTIVE / {XCDS} XCDs = {gpu_cycles:.4g} "
+              f"({gpu_cycles / (t['in_step_decode_us_mean'] * 1e-6) / 1e9:.2f} GHz over the traced in-step duration)",
+              f"- MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (kernel cycles x {num_cus} CUs x 4 SIMDs) = {mfma_busy:.4f}",
               f"- decode source sha256[:16] {source_sha()}", ""]
     with open(os.path.join(PROFILES, f"decode_kernel_{workload}.md"), "w") as f:
         f.write("\n".join(lines))
