@@ -10,9 +10,11 @@ shuffled block table).  The long-context workloads (one sequence of 1M tokens
 for MLA and MLRA-4, and the fp8 GLA-2 batch of imbalanced lengths) are timed
 in the same run and reported as sub-objects.
 
-Timing.  Before every timed step a 1 GiB scratch buffer is written (outside the
-timed events), which evicts the L2 caches and the 256 MB Infinity Cache, so
-every step reads its cache from HBM.  Each step is bracketed by HIP events on
+Timing.  Before every timed step a 1 GiB scratch buffer is read (a reduction,
+outside the timed events), which evicts the L2 caches and the 256 MB Infinity
+Cache, so every step reads its cache from HBM.  A read rather than a write: a
+1 GiB write flush leaves the Infinity Cache full of dirty lines, whose
+write-back then lands in the next step (it added ~37 us to the batch-64 step).  Each step is bracketed by HIP events on
 the stream the library launches on; the line reports the median and the
 10th/90th percentiles over the steps.  The decode kernel is timed inside the
 same step: ``ld_plan_decode`` (the step's first launch), an event, then
@@ -43,7 +45,7 @@ DECODE_SRC = [os.path.join(ROOT, "latent_kv_cache_absorbed_amd", "csrc", f) for 
 PROFILES = os.path.join(ROOT, "profiles")
 DEFAULT_WORKLOAD = "mla_b64_l4k"
 LONG_WORKLOADS = ("mla_b1_l1m", "mlra4_b1_l1m", "gla2_fp8_b64_mixed")
-FLUSH_BYTES = 1 << 30
+FLUSH_BYTES = 1 << 30         # scratch read before every timed step (4x the Infinity Cache)
 XCDS = 8                        # MI355X: 8 XCDs of 32 CUs
 
 
@@ -183,11 +185,9 @@ def measure(name, steps, warmup, min_warmup_ms, dev, flush, num_splits=0, stages
     torch.cuda.synchronize()
     gen_s = time.perf_counter() - t_gen
     stream = torch.cuda.current_stream(dev)
-    fill = [0]
 
     def do_flush():
-        fill[0] = (fill[0] + 1) & 0x7F
-        flush.fill_(fill[0])
+        torch.sum(flush, dtype=torch.int64)   # reads the whole buffer; leaves no dirty lines
 
     # warmup: W steps (each after a flush), continued until the GPU has been busy for min_warmup_ms
     # (its clocks take tens of milliseconds of load to settle)
@@ -417,7 +417,7 @@ def summarize_profile(workload: str, trace_dir: str, fetch_dir: str, write_dir: 
     lines = [f"# decode_kernel, workload {workload}", "",
              "Kernel durations (rocprofv3 kernel trace).  The decode kernel's in-step launches are its last",
              f"{2 * steps} dispatches: bench.py times {steps} steps as ld_latent_decode and {steps} as its two",
-             "launches with an event between; every step follows a 1 GiB flush write.", "",
+             "launches with an event between; every step follows a 1 GiB read of a scratch buffer.", "",
              f"    {commands[0]}", "",
              "| kernel | calls | mean us (all calls) | in-step mean us | in-step median us | min us | max us |",
              "|---|---|---|---|---|---|---|"]
@@ -485,7 +485,7 @@ def main() -> int:
 
     lkd.lib()
     dev = torch.device("cuda:0")
-    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+    flush = torch.zeros(FLUSH_BYTES // 4, dtype=torch.int32, device=dev)
     res, inp, d = measure(args.workload, args.steps, args.warmup, args.min_warmup_ms, dev, flush,
                           num_splits=args.num_splits, stages=args.stages, keep=True)
     stream = torch.cuda.current_stream(dev)
@@ -508,8 +508,8 @@ def main() -> int:
               "warmup_steps_run", "timed_region_s", "input_gen_s", "stages_back_to_back_ms"):
         if k in res:
             line[k] = res[k]
-    line["timing"] = ("per-step HIP events on the launch stream, a 1 GiB flush write before each step outside the "
-                      "events; value and ms_per_step from the median step")
+    line["timing"] = ("per-step HIP events on the launch stream, a 1 GiB read (reduction) before each step outside "
+                      "the events evicts L2 and the Infinity Cache; value and ms_per_step from the median step")
     if not args.no_parity:
         d.run()
         torch.cuda.synchronize()
