@@ -696,17 +696,13 @@ int launch_decode(const ld_problem& p, const DecodeArgs& a, void* stream) {
 }
 
 // Work groups of a shape's decode kernel that can be resident on one CU at once (registers, LDS,
-// waves), as the runtime reports it; 1 when it cannot be queried (no device).  Cached per shape.
+// waves), as the runtime reports it for the current device; 1 when it cannot be queried (no
+// device).  Cached per shape and device.
 template <int KV, int DL, int DR, int KIND, int NSETS, int HB, int SPLIT>
 int wgs_per_cu_of() {
-  static const int n = [] {
-    int v = 0;
-    const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-        &v, reinterpret_cast<const void*>(decode_kernel<KV, DL, DR, KIND, NSETS, HB, SPLIT>), NSETS * HB * SPLIT * kWaveSize,
-        0);
-    return (e == hipSuccess && v > 0) ? v : 1;
-  }();
-  return n;
+  static int cache[kMaxDevices] = {};  // 0: not queried yet
+  return occupancy_cached(cache, reinterpret_cast<const void*>(decode_kernel<KV, DL, DR, KIND, NSETS, HB, SPLIT>),
+                          NSETS * HB * SPLIT * kWaveSize);
 }
 
 int decode_wgs_per_cu(const ld_problem& p, int nsets, int hblocks) {
@@ -718,6 +714,18 @@ int decode_wgs_per_cu(const ld_problem& p, int nsets, int hblocks) {
   LD_SHAPES(LD_OCC)
 #undef LD_OCC
   return 1;
+}
+
+int occupancy_cached(int* cache, const void* kernel, int threads) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 1;
+  int v = __atomic_load_n(&cache[dev], __ATOMIC_RELAXED);
+  if (v > 0) return v;
+  int n = 0;
+  const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, threads, 0);
+  v = (e == hipSuccess && n > 0) ? n : 1;
+  __atomic_store_n(&cache[dev], v, __ATOMIC_RELAXED);  // every thread computes the same value
+  return v;
 }
 
 int device_cu_count() {

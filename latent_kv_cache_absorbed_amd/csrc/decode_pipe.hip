@@ -478,13 +478,8 @@ bool decode_pipe_serves(const ld_problem& p, int nsets, int hblocks) {
 }
 
 int decode_pipe_wgs_per_cu() {
-  static const int n = [] {
-    int v = 0;
-    const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-        &v, reinterpret_cast<const void*>(decode_pipe_kernel<512, 64, 4>), 4 * kWaveSize, 0);
-    return (e == hipSuccess && v > 0) ? v : 1;
-  }();
-  return n;
+  static int cache[kMaxDevices] = {};
+  return occupancy_cached(cache, reinterpret_cast<const void*>(decode_pipe_kernel<512, 64, 4>), 4 * kWaveSize);
 }
 
 }  // namespace ld

@@ -175,5 +175,10 @@ int decode_pipe_wgs_per_cu();
 bool decode_instantiated(const ld_problem& p, int nsets, int hblocks);
 int decode_wgs_per_cu(const ld_problem& p, int nsets, int hblocks);
 int device_cu_count();
+// Devices whose occupancy figures are cached (per kernel and device): device ids 0 .. kMaxDevices-1.
+constexpr int kMaxDevices = 64;
+// Resident work groups per CU of `kernel` with `threads` threads on the current device, from the
+// runtime's occupancy query, remembered in cache[device]; 1 when it cannot be queried.
+int occupancy_cached(int* cache, const void* kernel, int threads);
 
 }  // namespace ld

@@ -16,21 +16,19 @@ static __device__ __align__(256) char scratch[LD_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
-constexpr int kMaxDevices = 64;
-
 struct DeviceScratch {
   std::once_flag once;
   void* ptr = nullptr;
   hipError_t err = hipSuccess;
 };
-DeviceScratch g_scratch[kMaxDevices];
+DeviceScratch g_scratch[ld::kMaxDevices];
 
 // Device address of `scratch` on the current device (looked up on the first call on that device).
 hipError_t scratch_address(void** out) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
-  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  if (dev < 0 || dev >= ld::kMaxDevices) return hipErrorInvalidDevice;
   DeviceScratch& d = g_scratch[dev];
   std::call_once(d.once, [&d] {
     void* p = nullptr;
