@@ -41,7 +41,7 @@ METRIC = "decode-attn KV GB/s + tokens/s vs 1-GPU HBM/MFMA roofline, MLA 128h@4K
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
 MFMA_F32_PEAK_TFLOPS = 157.3
-DECODE_SRC = [os.path.join(ROOT, "latent_kv_cache_absorbed_amd", "csrc", f) for f in ("decode.hip", "decode_common.h", "plan_common.h")]
+DECODE_SRC = [os.path.join(ROOT, "latent_kv_cache_absorbed_amd", "csrc", f) for f in ("decode.hip", "decode_pipe.hip", "decode_common.h", "plan_common.h")]
 PROFILES = os.path.join(ROOT, "profiles")
 DEFAULT_WORKLOAD = "mla_b64_l4k"
 LONG_WORKLOADS = ("mla_b1_l1m", "mlra4_b1_l1m", "gla2_fp8_b64_mixed")
