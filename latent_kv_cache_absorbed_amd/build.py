@@ -19,8 +19,8 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "liblatent_decode.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["api.cpp", "plan_combine.hip", "decode.hip", "decode_pipe.hip", "append.hip", "projection.hip",
-           "noalloc.hip"]
+SOURCES = ["api.cpp", "plan_combine.hip", "decode.hip", "decode_pipe.hip", "decode_pipe_fp8.hip", "append.hip",
+           "projection.hip", "noalloc.hip"]
 
 COMMON = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-I", INCLUDE, "-I", CSRC,
           # packed fp32 VALU forms are kept out of every kernel
@@ -30,7 +30,8 @@ COMMON = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-I", INCLUDE, 
 # waves per SIMD this avoids AGPR round trips and spills; the pipelined kernel's own P.V accumulators
 # sit in AGPRs through inline asm).
 EXTRA = {"decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
-         "decode_pipe.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+         "decode_pipe.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+         "decode_pipe_fp8.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def _compile(src: str, extra) -> str:

@@ -295,7 +295,7 @@ int32_t check_pointers(const ld_problem* p, const void* q_latent, const void* q_
       !aligned(lse, 4) || !aligned(block_table, 4) || !aligned(seq_lens, 4))
     return LD_ERR_MISALIGNED;
   if (cache->v && !aligned(cache->v, 16)) return LD_ERR_MISALIGNED;
-  if (fp8 && (!aligned(cache->rope, 16) || !aligned(cache->scale, 4))) return LD_ERR_MISALIGNED;
+  if (fp8 && (!aligned(cache->rope, 16) || !aligned(cache->scale, 16))) return LD_ERR_MISALIGNED;
   return LD_OK;
 }
 

@@ -686,6 +686,7 @@ bool decode_instantiated(const ld_problem& p, int nsets, int hblocks) {
 
 int launch_decode(const ld_problem& p, const DecodeArgs& a, void* stream) {
   if (decode_pipe_serves(p, a.nsets, a.hblocks)) return launch_decode_pipe(p, a, stream);
+  if (decode_pipe8_serves(p, a.nsets, a.hblocks)) return launch_decode_pipe8(p, a, stream);
   const int kv = kv_code(p), kind = kind_code(p), dl = p.d_latent, dr = p.d_rope;
 #define LD_RUN(KV_, DL_, DR_, KIND_, NS_, HB_, SP_)                                               \
   if (kv == KV_ && dl == DL_ && dr == DR_ && kind == KIND_ && a.nsets == NS_ && a.hblocks == HB_) \
@@ -707,6 +708,7 @@ int wgs_per_cu_of() {
 
 int decode_wgs_per_cu(const ld_problem& p, int nsets, int hblocks) {
   if (decode_pipe_serves(p, nsets, hblocks)) return decode_pipe_wgs_per_cu();
+  if (decode_pipe8_serves(p, nsets, hblocks)) return decode_pipe8_wgs_per_cu(p);
   const int kv = kv_code(p), kind = kind_code(p), dl = p.d_latent, dr = p.d_rope;
 #define LD_OCC(KV_, DL_, DR_, KIND_, NS_, HB_, SP_) \
   if (kv == KV_ && dl == DL_ && dr == DR_ && kind == KIND_ && nsets == NS_ && hblocks == HB_) \

@@ -47,6 +47,26 @@ __device__ __forceinline__ void wait_vmcnt() {
 // pipeline; here the caller waits for exactly the copies it needs (wait_vmcnt) first.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
+// The pipelined kernels (decode_pipe.hip, decode_pipe_fp8.hip) use a fixed softmax reference per
+// unit: p = 2^(s - r) may reach 2^kRefSlack before the unit is run again with the exact max, far
+// below the fp32 / bf16 range, so sums of up to 2^20 stages x 32 tokens of such values stay finite.
+constexpr float kRefSlack = 64.f;
+
+// P.V MFMA accumulating into AGPRs.  The pipelined kernels' score MFMAs are compiler builtins with
+// their results in VGPRs (the softmax reads them), and one function holds one MFMA register form,
+// so the P.V MFMAs, whose accumulators sit in the AGPRs, are written out.
+__device__ __forceinline__ void mfma_pv(floatx16& acc, bf16x8_t a, bf16x8_t b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+// The same MFMA for an A operand computed by VALU instructions just before it (the fp8 values
+// converted to bf16): the compiler inserts no wait states ahead of an inline-asm MFMA, so the
+// VALU-write -> MFMA-read distance the hardware needs is written out.
+__device__ __forceinline__ void mfma_pv_valu_a(floatx16& acc, bf16x8_t a, bf16x8_t b) {
+  asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+// Wait states after the last P.V MFMA before its accumulators are read or rewritten.
+__device__ __forceinline__ void mfma_pv_drain() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); }
+
 // 16-byte global -> LDS copy per lane; the LDS destination of lane i is lds + 16 i.
 __device__ __forceinline__ void dma16(const char* base, unsigned voff, char* lds_wave_base) {
   __builtin_amdgcn_global_load_lds(base + voff, (__attribute__((address_space(3))) void*)(lds_wave_base), 16, 0, 0);
@@ -59,9 +79,8 @@ __device__ __forceinline__ void dma16(const char* base, unsigned voff, char* lds
 // counts in vmcnt only, and nothing of it is visible to the compiler: a kernel that uses it waits for
 // its copies itself (wait_vmcnt, then a barrier) before any wave reads the stage, and uses M0 for
 // nothing else.  lds_wave_base must be a direct pointer into a __shared__ array (so that its LDS
-// address folds to a constant plus an offset).
-__device__ __forceinline__ void dma16_asm(const char* base, unsigned voff, char* lds_wave_base) {
-  const unsigned lds = (unsigned)(uintptr_t)(__attribute__((address_space(3))) char*)(lds_wave_base);
+// address folds to a constant plus an offset); dma16_asm_at takes that LDS address as a number.
+__device__ __forceinline__ void dma16_asm_at(const char* base, unsigned voff, unsigned lds) {
   const unsigned long long b = (unsigned long long)(uintptr_t)base;
   const unsigned long long bs = ((unsigned long long)__builtin_amdgcn_readfirstlane((unsigned)(b >> 32)) << 32) |
                                 (unsigned)__builtin_amdgcn_readfirstlane((unsigned)b);
@@ -72,6 +91,9 @@ __device__ __forceinline__ void dma16_asm(const char* base, unsigned voff, char*
                : "v"(voff), "s"(__builtin_amdgcn_readfirstlane(lds)), "s"(bs)
                : "memory", "m0");
 #pragma clang diagnostic pop
+}
+__device__ __forceinline__ void dma16_asm(const char* base, unsigned voff, char* lds_wave_base) {
+  dma16_asm_at(base, voff, (unsigned)(uintptr_t)(__attribute__((address_space(3))) char*)(lds_wave_base));
 }
 
 // ------------------------------------------------------------------------------------------

@@ -29,10 +29,6 @@
 namespace ld {
 namespace {
 
-// p = 2^(s - r) may reach 2^kRefSlack before the unit is run again with the exact max: far below
-// the fp32 / bf16 range, so sums of up to 2^20 stages x 32 tokens of such values stay finite.
-constexpr float kRefSlack = 64.f;
-
 template <int DL, int DR, int HB>
 struct PCfg {
   using M = Mma<KV_BF16>;
@@ -60,15 +56,6 @@ struct PCfg {
   static_assert(pow2(LW) && pow2(RW) && (kTile * RW) % 1024 == 0, "row sizes");
   static_assert(NBUF * BUF + 4 * kUnitPages + 64 <= 160 * 1024, "LDS budget");
 };
-
-// P.V MFMA accumulating into AGPRs.  The score MFMAs of this kernel are compiler builtins with their
-// results in VGPRs (the softmax reads them), and one function holds one MFMA register form, so the
-// P.V MFMAs, whose 256 accumulators fill the AGPRs, are written out.
-__device__ __forceinline__ void mfma_pv(floatx16& acc, bf16x8_t a, bf16x8_t b) {
-  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
-}
-// Wait states after the last P.V MFMA before its accumulators are read or rewritten.
-__device__ __forceinline__ void mfma_pv_drain() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); }
 
 template <int DL, int DR, int HB>
 __global__ __launch_bounds__(HB * 64) void decode_pipe_kernel(DecodeArgs a, const int32_t* __restrict__ block_table) {
