@@ -27,6 +27,13 @@ Shape launch_shape(const ld_problem& p) {
   const int H = p.num_q_heads, G = p.num_groups;
   s.heads_per_set = p.variant == LD_VARIANT_MLRA ? H : H / G;
   s.hblocks = (s.heads_per_set + 31) / 32;
+  // fp8 GLA groups of 64 heads: one group per work group (two work groups of four waves share a CU,
+  // and their barriers do not hold each other up)
+  if (decode_pipe8_serves(p, 1, s.hblocks) && decode_instantiated(p, 1, s.hblocks)) {
+    s.nsets = 1;
+    s.wg_per_unit = G * p.q_len;
+    return s;
+  }
   for (int n = 8; n >= 1; n >>= 1) {
     if (G % n) continue;
     if (!decode_instantiated(p, n, s.hblocks)) continue;

@@ -170,11 +170,11 @@ int launch_head_projection(const ProjArgs& a, int out_bf16, void* stream);
 bool decode_pipe_serves(const ld_problem& p, int nsets, int hblocks);
 int launch_decode_pipe(const ld_problem& p, const DecodeArgs& a, void* stream);
 int decode_pipe_wgs_per_cu();
-// The software-pipelined kernel for fp8 latent caches (decode_pipe_fp8.hip): 256-dim latent groups
-// with a 64-dim RoPE key, 64 heads per group, every group (one or two) in one work group.
+// The kernel for fp8 latent caches (decode_pipe_fp8.hip): 256-dim latent groups with a 64-dim RoPE
+// key, 64 heads per group, one or two groups per work group.
 bool decode_pipe8_serves(const ld_problem& p, int nsets, int hblocks);
 int launch_decode_pipe8(const ld_problem& p, const DecodeArgs& a, void* stream);
-int decode_pipe8_wgs_per_cu(const ld_problem& p);
+int decode_pipe8_wgs_per_cu(int nsets);
 // Whether a decode kernel is built for p's dtype/dims/kind with `nsets` sets per work group and
 // `hblocks` 32-head blocks per set.
 bool decode_instantiated(const ld_problem& p, int nsets, int hblocks);
