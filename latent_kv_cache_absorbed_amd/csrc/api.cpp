@@ -79,7 +79,7 @@ WsLayout ws_layout(const ld_problem& p, int num_cus) {
   const size_t pieces = (size_t)query_sets(p) * launch_shape(p).hblocks * (w.d_v / 32) * (16 / vals) * 64;
   w.xblocks = (int32_t)(pieces / 256);
   w.tasks = off;
-  off = round256(off + (size_t)w.max_tasks * 2 * sizeof(int32_t));
+  off = round256(off + (size_t)w.max_tasks * 4 * sizeof(int32_t));
   // a sequence merged in more than one chunk has more than kCombineChunk units
   w.max_multi = p.num_splits > 0 ? (n_forced > kCombineChunk ? p.batch : 0)
                                  : std::min<int32_t>(p.batch, w.max_units / (kCombineChunk + 1));

@@ -47,7 +47,7 @@ struct WsLayout {
   size_t header = 0;       // int32[64]: [0] num_units, [1] chunk
   size_t units = 0;        // Unit[max_units]
   size_t seqs = 0;         // int32[4*B]: (num_splits, first_unit, first_task, num_tasks) per sequence
-  size_t tasks = 0;        // int32[2*max_tasks]: (sequence, chunk) combine tasks
+  size_t tasks = 0;        // int32[4*max_tasks]: (sequence, chunk, first_unit, num_splits) combine tasks
   size_t multi = 0;        // int32[max_multi]: sequences merged in more than one chunk
   size_t l2_out = 0;       // f32[max_tasks][pieces][values]: chunk results of multi-chunk sequences
   size_t l2_lse = 0;       // f32[max_tasks][pieces]: their lse, per piece lane

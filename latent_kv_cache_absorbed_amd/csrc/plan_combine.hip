@@ -91,8 +91,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
       a.seqs[4 * b + 3] = nc;
       for (int c = 0; c < nc; ++c)
         if (ftask + c < a.max_tasks) {
-          a.tasks[2 * (ftask + c)] = b;
-          a.tasks[2 * (ftask + c) + 1] = c;
+          reinterpret_cast<int4*>(a.tasks)[ftask + c] = make_int4(b, c, first, n);
         }
       if (mc && mi < a.max_multi) a.multi[mi] = b;
       for (int s = 0; s < n && s < kOwnUnits; ++s) write_unit(b, s, first, L, ck);
@@ -309,14 +308,16 @@ __global__ __launch_bounds__(kCombineThreads) void combine_ws_kernel(DecodeArgs 
   __shared__ float tile[32 * 65];
   const int t = blockIdx.y;
   // the task record (in bounds for every t < max_tasks) is read together with the task count
+  // The task record carries what the merge needs (sequence, chunk, first unit, splits), so the
+  // partials' loads wait for one round trip, not two; it is read together with the task count.
   const int ntask = a.header[2];
-  const int b = a.tasks[2 * t];
-  const int c = a.tasks[2 * t + 1];
+  const int4 task = reinterpret_cast<const int4*>(a.tasks)[t];
+  const int b = task.x, c = task.y;
   if ((t >= ntask) | (b < 0)) return;  // (b >= 0 in every task; testing it keeps both loads before the branch)
-  const int first = a.seqs[4 * b + 1];
-  const int n = max(0, min(a.seqs[4 * b], a.max_units - first));
-  const int ftask = a.seqs[4 * b + 2];
-  const int nc = a.seqs[4 * b + 3];
+  const int first = task.z;
+  const int n = max(0, min(task.w, a.max_units - first));
+  const int nc = task.w > kCombineChunk ? (task.w + kCombineChunk - 1) / kCombineChunk : 1;
+  const int ftask = t - c;
   const int pg = 4 * blockIdx.x + (threadIdx.x >> 6);
   const PieceGroup p = piece_group(a, d_v, pg);
   const int vals = a.part_bf16 ? 8 : 4;

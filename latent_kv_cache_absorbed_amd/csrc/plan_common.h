@@ -191,10 +191,7 @@ __device__ __forceinline__ void fused_plan_unit(const DecodeArgs& a, int x, int 
         P.seqs[4 * b + 1] = cn + in;
         P.seqs[4 * b + 2] = ftask;
         P.seqs[4 * b + 3] = 1;
-        if (ftask < P.max_tasks) {
-          P.tasks[2 * ftask] = b;
-          P.tasks[2 * ftask + 1] = 0;
-        }
+        if (ftask < P.max_tasks) reinterpret_cast<int4*>(P.tasks)[ftask] = make_int4(b, 0, cn + in, 0);
       }
       cn += __shfl(in, 63);
       cc += __shfl(ic, 63);
@@ -256,10 +253,7 @@ __device__ __forceinline__ void fused_plan_unit(const DecodeArgs& a, int x, int 
     if (mc && mi < P.max_multi) P.multi[mi] = b;
   }
   for (int c = lane; c < nc; c += 64) {
-    if (ftask + c < P.max_tasks) {
-      P.tasks[2 * (ftask + c)] = b;
-      P.tasks[2 * (ftask + c) + 1] = c;
-    }
+    if (ftask + c < P.max_tasks) reinterpret_cast<int4*>(P.tasks)[ftask + c] = make_int4(b, c, first, n);
   }
 }
 
