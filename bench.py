@@ -41,7 +41,8 @@ METRIC = "decode-attn KV GB/s + tokens/s vs 1-GPU HBM/MFMA roofline, MLA 128h@4K
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
 MFMA_F32_PEAK_TFLOPS = 157.3
-DECODE_SRC = [os.path.join(ROOT, "latent_kv_cache_absorbed_amd", "csrc", f) for f in ("decode.hip", "decode_pipe.hip", "decode_common.h", "plan_common.h")]
+DECODE_SRC = [os.path.join(ROOT, "latent_kv_cache_absorbed_amd", "csrc", f)
+              for f in ("decode.hip", "decode_pipe.hip", "decode_pipe_fp8.hip", "decode_common.h", "plan_common.h")]
 PROFILES = os.path.join(ROOT, "profiles")
 DEFAULT_WORKLOAD = "mla_b64_l4k"
 LONG_WORKLOADS = ("mla_b1_l1m", "mlra4_b1_l1m", "gla2_fp8_b64_mixed")
@@ -259,8 +260,7 @@ def measure(name, steps, warmup, min_warmup_ms, dev, flush, num_splits=0, stages
         "tokens_per_s": round(inp.batch * inp.q_len / t_med, 1),
         "kv_tokens_per_s": round(float(lens.sum()) / t_med, 1),
         "hbm_frac_step": round((kv_bytes + q_bytes + out_bytes) / t_med / 1e9 / HBM_PEAK_GBS, 4),
-        "roofline": {"kernel": "decode_pipe_kernel" if (w.variant == "mla" and inp.kv_dtype == "bf16" and inp.heads == 128)
-                     else "decode_kernel", "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+        "roofline": {"kernel": decode_kernel_name(w, inp), "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": None if prof is None else prof.get("hbm_bytes_per_launch"),
                      "traffic_source": None if prof is None else os.path.relpath(traffic_path(name), ROOT),
@@ -367,8 +367,19 @@ def _counter(dir_: str, name: str):
 
 
 def is_decode(kernel_name: str) -> bool:
-    """The decode kernels (decode_kernel of decode.hip, decode_pipe_kernel of decode_pipe.hip)."""
-    return "decode_kernel" in kernel_name or "decode_pipe_kernel" in kernel_name
+    """The decode kernels (decode_kernel of decode.hip, decode_pipe_kernel of decode_pipe.hip,
+    decode_pipe8_kernel of decode_pipe_fp8.hip)."""
+    return any(k in kernel_name for k in ("decode_kernel", "decode_pipe_kernel", "decode_pipe8_kernel"))
+
+
+def decode_kernel_name(w, inp) -> str:
+    """The kernel the library launches for a workload's decode (its dispatch rule, restated)."""
+    if w.variant == "mla" and inp.kv_dtype == "bf16" and inp.heads == 128 and inp.d_lat == 512 and inp.d_rope == 64:
+        return "decode_pipe_kernel"
+    if (inp.kv_dtype == "fp8_e4m3" and w.variant in ("mla", "gla") and inp.d_lat == 256 and inp.d_rope == 64
+            and inp.heads == 64 * inp.groups and inp.groups in (1, 2)):
+        return "decode_pipe8_kernel"
+    return "decode_kernel"
 
 
 def summarize_profile(workload: str, trace_dir: str, fetch_dir: str, write_dir: str, mfma_dir: str, copy_mib: int,
