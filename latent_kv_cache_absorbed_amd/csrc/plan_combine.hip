@@ -234,6 +234,43 @@ struct Merge {
     }
     M = Mn;
   }
+  // the same over raw pieces as loaded: eight bf16 (bf16 = true) or four f32 per uint4, widened
+  // here, so that a batch of loads in flight holds 4 registers a piece, not 8 (more work groups fit)
+  template <int KB = kBatch>
+  __device__ __forceinline__ void add_raw(const float* ls, const uint4* raw, int valid, bool bf16) {
+    float bm = -INFINITY;
+    bool nan = false;
+#pragma unroll
+    for (int k = 0; k < KB; ++k)
+      if (k < valid) {
+        bm = fmaxf(bm, ls[k]);
+        nan |= ls[k] != ls[k];
+      }
+    if (nan) tot = __builtin_nanf("");
+    const float Mn = fmaxf(M, bm);
+    if (Mn == -INFINITY) return;
+    const float r = (M == -INFINITY) ? 0.f : wexp(M - Mn);
+    tot *= r;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] *= r;
+#pragma unroll
+    for (int k = 0; k < KB; ++k) {
+      const float w = k < valid ? wexp(ls[k] - Mn) : 0.f;
+      tot += w;
+      const unsigned u[4] = {raw[k].x, raw[k].y, raw[k].z, raw[k].w};
+      if (bf16) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          o[2 * q] += w * __builtin_bit_cast(float, u[q] << 16);
+          o[2 * q + 1] += w * __builtin_bit_cast(float, u[q] & 0xffff0000u);
+        }
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) o[q] += w * __builtin_bit_cast(float, u[q]);
+      }
+    }
+    M = Mn;
+  }
   // fold in another state (its pairs come after this one's)
   __device__ __forceinline__ void merge(float M2, float tot2, const float* o2) {
     if (tot2 != tot2) tot = __builtin_nanf("");
@@ -307,7 +344,6 @@ __device__ __forceinline__ void write_tile(const DecodeArgs& a, int d_v, const P
 __global__ __launch_bounds__(kCombineThreads) void combine_ws_kernel(DecodeArgs a, int d_v) {
   __shared__ float tile[32 * 65];
   const int t = blockIdx.y;
-  // the task record (in bounds for every t < max_tasks) is read together with the task count
   // The task record carries what the merge needs (sequence, chunk, first unit, splits), so the
   // partials' loads wait for one round trip, not two; it is read together with the task count.
   const int ntask = a.header[2];
@@ -327,24 +363,17 @@ __global__ __launch_bounds__(kCombineThreads) void combine_ws_kernel(DecodeArgs 
   // one batch of KB (lse, piece) pairs, loads issued together; indexes past the last repeat it
   auto batch = [&](auto kb, int k0) {
     constexpr int KB = decltype(kb)::value;
-    float ls[KB], v[KB][8];
+    float ls[KB];
+    uint4 raw[KB];
 #pragma unroll
     for (int k = 0; k < KB; ++k) {
       const size_t s = first + s_lo + min(k0 + k, cnt - 1);
       ls[k] = a.part_lse[(s * p.blocks_per_unit + p.blk_in_unit) * 32 + (p.lane & 31)];
       const size_t off = (s * p.blocks_per_unit + p.blk_in_unit) * (size_t)(32 * d_v) + p.piece_off;
-      if (a.part_bf16) {
-        typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-        const bf16x8_t x = *reinterpret_cast<const bf16x8_t*>(static_cast<const __bf16*>(a.part_out) + off);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[k][e] = (float)x[e];
-      } else {
-        const float4 x = *reinterpret_cast<const float4*>(static_cast<const float*>(a.part_out) + off);
-        v[k][0] = x.x, v[k][1] = x.y, v[k][2] = x.z, v[k][3] = x.w;
-        v[k][4] = v[k][5] = v[k][6] = v[k][7] = 0.f;
-      }
+      raw[k] = a.part_bf16 ? *reinterpret_cast<const uint4*>(static_cast<const __bf16*>(a.part_out) + off)
+                           : *reinterpret_cast<const uint4*>(static_cast<const float*>(a.part_out) + off);
     }
-    m.add<KB>(ls, v, cnt - k0, vals);
+    m.add_raw<KB>(ls, raw, cnt - k0, a.part_bf16 != 0);
   };
   if (cnt <= 4) {
     if (cnt > 0) batch(std::integral_constant<int, 4>{}, 0);
@@ -379,10 +408,11 @@ __global__ __launch_bounds__(kCombineThreads) void combine_ws_kernel(DecodeArgs 
   if (!s_last) return;
   __threadfence();
   Merge mm;
-  for (int q0 = 0; q0 < nc; q0 += kBatch) {
-    float ls[kBatch], v[kBatch][8];
+  constexpr int kB2 = 4;  // (chunk results are f32: eight registers a piece)
+  for (int q0 = 0; q0 < nc; q0 += kB2) {
+    float ls[kB2], v[kB2][8];
 #pragma unroll
-    for (int k = 0; k < kBatch; ++k) {
+    for (int k = 0; k < kB2; ++k) {
       const size_t l2 = (size_t)(ftask + min(q0 + k, nc - 1)) * p.pieces + (size_t)pg * 64 + p.lane;
       ls[k] = a.l2_lse[l2];
       const float4* src = reinterpret_cast<const float4*>(a.l2_out + l2 * vals);
@@ -391,7 +421,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_ws_kernel(DecodeArgs 
       v[k][0] = x0.x, v[k][1] = x0.y, v[k][2] = x0.z, v[k][3] = x0.w;
       v[k][4] = x1.x, v[k][5] = x1.y, v[k][6] = x1.z, v[k][7] = x1.w;
     }
-    mm.add(ls, v, nc - q0, vals);
+    mm.add<kB2>(ls, v, nc - q0, vals);
   }
   write_piece(a, d_v, p, b, mm.o, mm.finish());
 }
