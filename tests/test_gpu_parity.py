@@ -63,6 +63,13 @@ def test_mla_bf16_small_heads():
     _check(inp)
 
 
+def test_mla_bf16_partial_head_block():
+    # 112 heads: the 128-head work group holds 16 absent heads, whose query rows it must neither read
+    # past the last sequence's rows nor let into the result
+    inp = synth.make_inputs("mla", 3, 112, 1, 512, 64, [300, 4097, 33], scale=1 / math.sqrt(192), seed=17)
+    _check(inp)
+
+
 # --- GLA-2 (bf16 and fp8) and MLRA-4
 @pytest.mark.parametrize("kv", ["bf16", "fp8_e4m3"])
 def test_gla2(kv):
