@@ -376,6 +376,9 @@ def decode_kernel_name(w, inp) -> str:
     """The kernel the library launches for a workload's decode (its dispatch rule, restated)."""
     if w.variant == "mla" and inp.kv_dtype == "bf16" and inp.heads == 128 and inp.d_lat == 512 and inp.d_rope == 64:
         return "decode_pipe_kernel"
+    if (w.variant == "mlra" and inp.kv_dtype == "bf16" and inp.heads == 128 and inp.d_lat == 128 and inp.d_rope == 64
+            and inp.groups in (1, 4)):
+        return "decode_pipe_kernel"
     if (inp.kv_dtype == "fp8_e4m3" and w.variant in ("mla", "gla") and inp.d_lat == 256 and inp.d_rope == 64
             and inp.heads == 64 * inp.groups and inp.groups in (1, 2)):
         return "decode_pipe8_kernel"

@@ -34,6 +34,12 @@ Shape launch_shape(const ld_problem& p) {
     s.wg_per_unit = G * p.q_len;
     return s;
   }
+  // bf16 MLRA: one branch of 128 heads per work group (the pipelined kernel)
+  if (p.variant == LD_VARIANT_MLRA && decode_pipe_serves(p, 1, s.hblocks) && decode_instantiated(p, 1, s.hblocks)) {
+    s.nsets = 1;
+    s.wg_per_unit = G * p.q_len;
+    return s;
+  }
   for (int n = 8; n >= 1; n >>= 1) {
     if (G % n) continue;
     if (!decode_instantiated(p, n, s.hblocks)) continue;

@@ -707,7 +707,7 @@ int wgs_per_cu_of() {
 }
 
 int decode_wgs_per_cu(const ld_problem& p, int nsets, int hblocks) {
-  if (decode_pipe_serves(p, nsets, hblocks)) return decode_pipe_wgs_per_cu();
+  if (decode_pipe_serves(p, nsets, hblocks)) return decode_pipe_wgs_per_cu(p);
   if (decode_pipe8_serves(p, nsets, hblocks)) return decode_pipe8_wgs_per_cu(nsets);
   const int kv = kv_code(p), kind = kind_code(p), dl = p.d_latent, dr = p.d_rope;
 #define LD_OCC(KV_, DL_, DR_, KIND_, NS_, HB_, SP_) \

@@ -29,10 +29,12 @@
 namespace ld {
 namespace {
 
-template <int DL, int DR, int HB>
+template <int DL, int DR, int HB, int G>
 struct PCfg {
   using M = Mma<KV_BF16>;
   static constexpr int WAVES = HB;
+  static constexpr int GROW = G * DL * 2 + DR * 2;   // cached row bytes: G latent slices, then the rope key
+  static constexpr int ROPE_COL = G * DL * 2;        // byte offset of the rope key in a cached row
   static constexpr int THREADS = WAVES * kWaveSize;
   static constexpr int KL = DL / 16;                 // latent k-steps of S
   static constexpr int KR = DR / 16;                 // rope k-steps of S
@@ -48,18 +50,30 @@ struct PCfg {
   static constexpr int NBUF = 4;
   static constexpr int DMA_BLOCKS = kTile * (LW + RW) / 1024;
   static constexpr int DMA_PER_WAVE = DMA_BLOCKS / WAVES;
+  static constexpr int LPW = kTile * LW / 1024 / WAVES;   // latent copies per wave and stage
+  static constexpr int NGS = KS / 4;                     // groups of four score MFMAs per stage
   static constexpr int NKL = (MLS + 1) / 2;          // latent k-steps per swizzle group
   static constexpr int NVT = (MLS >> 2) + 1;          // V column blocks per swizzle group
   static_assert(DMA_BLOCKS % WAVES == 0, "every wave issues the same number of copies");
   static_assert(KS % 4 == 0 && CB % 4 == 0, "k-steps and column blocks come in groups of four");
+  static_assert((kTile * LW / 1024) % WAVES == 0 && kTile * RW == 1024 * WAVES, "copy dealing: one rope block per wave");
+  static_assert(NGS == 9 || NGS == 3, "the softmax is laid out over nine or three score groups");
+  // Where the copies of stage n + 3 go in iteration n (a copy instruction holds up the wave that
+  // issues it, so they are paced rather than issued in a burst).  576-dim rows: nine copies, one per
+  // two groups of MFMAs (five among the nine score groups, four among the eight P.V groups).
+  // 192-dim rows: three copies, one after each of the three score groups.
+  static constexpr __device__ bool copy_after_score(int g) { return NGS == 9 ? (g & 1) == 0 : true; }
+  static constexpr __device__ int score_copy(int g) { return NGS == 9 ? g / 2 : g; }
+  static constexpr __device__ bool copy_after_pv(int g) { return NGS == 9 ? (g & 1) != 0 : false; }
+  static constexpr __device__ int pv_copy(int g) { return 5 + g / 2; }
   static_assert(2 * KR <= MR + 1, "rope row must lie in one swizzle group");
   static_assert(pow2(LW) && pow2(RW) && (kTile * RW) % 1024 == 0, "row sizes");
   static_assert(NBUF * BUF + 4 * kUnitPages + 64 <= 160 * 1024, "LDS budget");
 };
 
-template <int DL, int DR, int HB>
-__global__ __launch_bounds__(HB * 64) void decode_pipe_kernel(DecodeArgs a, const int32_t* __restrict__ block_table) {
-  using C = PCfg<DL, DR, HB>;
+template <int DL, int DR, int HB, int G, int MINB>
+__global__ __launch_bounds__(HB * 64, MINB) void decode_pipe_kernel(DecodeArgs a, const int32_t* __restrict__ block_table) {
+  using C = PCfg<DL, DR, HB, G>;
   using M = typename C::M;
   __shared__ __attribute__((aligned(128))) char lds_b0[C::BUF];
   __shared__ __attribute__((aligned(128))) char lds_b1[C::BUF];
@@ -97,10 +111,11 @@ __global__ __launch_bounds__(HB * 64) void decode_pipe_kernel(DecodeArgs a, cons
     t_end = u.t_end;
     nsplit = a.seqs[4 * b];
   }
-  // query token qi of the unit's work groups (several query tokens: token qi sees the first
-  // L_b - qlen + 1 + qi rows); one set (the whole head set of the latent row)
-  const int qi = sb;
-  const int gs = qi * a.cache_groups;
+  // query token qi and latent slice `branch` of the work group (several query tokens: token qi sees
+  // the first L_b - qlen + 1 + qi rows); query set gs = qi * G + branch (MLA: one slice, G = 1)
+  const int qi = sb / G;
+  const int branch = sb - qi * G;
+  const int gs = qi * G + branch;
   if (a.qlen > 1) {
     const int Lb = clampi(a.seq_lens[b], 0, a.max_pages * a.page_size);
     t_end = max(t_begin, min(t_end, Lb - a.qlen + 1 + qi));
@@ -112,7 +127,7 @@ __global__ __launch_bounds__(HB * 64) void decode_pipe_kernel(DecodeArgs a, cons
   const int hb = wave;
   const int head_in_set = hb * 32 + col;
   const bool valid = head_in_set < a.heads_per_set;
-  const int head = gs * a.heads_per_set + (valid ? head_in_set : 0);
+  const int head = qi * a.heads_per_set + (valid ? head_in_set : 0);
   const int32_t* __restrict__ bt_row = block_table + (size_t)b * a.max_pages;
   const int page_size = a.page_size;
   const int first_page = t_begin / page_size;
@@ -121,11 +136,13 @@ __global__ __launch_bounds__(HB * 64) void decode_pipe_kernel(DecodeArgs a, cons
     lds_pages[i] = clampi(bt_row[first_page + i], 0, a.num_pages - 1);
   __syncthreads();
 
-  const int grow_bytes = DL * 2 + DR * 2;
+  const int grow_bytes = C::GROW;
+  const int lat_col = branch * (DL * 2);  // byte offset of the work group's latent slice in a cached row
   const char* kbase = static_cast<const char*>(a.k);
-  // Stage copies.  Wave w copies 1 KB blocks w, w + 4, .., w + 28 of the latent region and block w of
-  // the rope region (the dealing of dma_region): copy j < 8 is latent block w + 4 j, copy 8 the rope
-  // block.  The stage's rows come from one page: its id is read from LDS once per stage.
+  // Stage copies.  Wave w copies 1 KB blocks w, w + 4, .. of the latent region and block w of the
+  // rope region (the dealing of dma_region): copy j < LPW is latent block w + 4 j (LPW = 8 for a
+  // 512-dim slice, 2 for a 128-dim one), copy LPW the rope block.  The stage's rows come from one
+  // page: its id is read from LDS once per stage.
   struct StageSrc {
     const char* rows;
     int tlast;
@@ -141,7 +158,7 @@ __global__ __launch_bounds__(HB * 64) void decode_pipe_kernel(DecodeArgs a, cons
     // loop invariant), so they do not hold registers across the loop
     int ln = lane;
     asm volatile("" : "+v"(ln));
-    if (j < 8) {
+    if (j < C::LPW) {
       const int q = wave + C::WAVES * j;
       constexpr int CPR = C::LW / 16;
       const int t = (q * 1024) / C::LW + ln / CPR;
@@ -149,7 +166,7 @@ __global__ __launch_bounds__(HB * 64) void decode_pipe_kernel(DecodeArgs a, cons
       const int c = (cp & ~C::MLS) | ((cp & C::MLS) ^ (swz_key(t) & C::MLS));
       const int tf = (q * 1024) / C::LW;
       const int tu = min(tf, src.tlast);
-      unsigned voff = (unsigned)((min(t, src.tlast) - tu) * grow_bytes + (c << 4));
+      unsigned voff = (unsigned)((min(t, src.tlast) - tu) * grow_bytes + lat_col + (c << 4));
       asm volatile("" : "+v"(voff));
       dma16_asm(src.rows + (size_t)tu * grow_bytes, voff, buf + q * 1024);
     } else {
@@ -160,7 +177,7 @@ __global__ __launch_bounds__(HB * 64) void decode_pipe_kernel(DecodeArgs a, cons
       const int c = (cp & ~C::MR) | ((cp & C::MR) ^ (swz_key(t) & C::MR));
       const int tf = (q * 1024) / C::RW;
       const int tu = min(tf, src.tlast);
-      unsigned voff = (unsigned)((min(t, src.tlast) - tu) * grow_bytes + DL * 2 + (c << 4));
+      unsigned voff = (unsigned)((min(t, src.tlast) - tu) * grow_bytes + C::ROPE_COL + (c << 4));
       asm volatile("" : "+v"(voff));
       dma16_asm(src.rows + (size_t)tu * grow_bytes, voff, buf + C::ROPE_OFF + q * 1024);
     }
@@ -170,12 +187,11 @@ __global__ __launch_bounds__(HB * 64) void decode_pipe_kernel(DecodeArgs a, cons
 #pragma unroll
     for (int j = 0; j < C::DMA_PER_WAVE; ++j) copy_block(src, buf, j);
   };
-  static_assert(C::DMA_PER_WAVE == 9 && C::DMA_BLOCKS == 36 && C::LW == 1024, "copy dealing of the 576-dim row");
 
   // this lane's query fragments (B operand of S^T = K . Q^T): all latent and rope k-steps
   bf16x8_t qf[C::KS];
   {
-    const size_t qrow = (size_t)b * a.heads + head;
+    const size_t qrow = ((size_t)b * a.heads + head) * G + branch;
     const __bf16* qlp = static_cast<const __bf16*>(a.q_lat) + qrow * DL + h * 8;
     const __bf16* qrp = static_cast<const __bf16*>(a.q_rope) + qrow * DR + h * 8;
 #pragma unroll
@@ -225,8 +241,9 @@ __global__ __launch_bounds__(HB * 64) void decode_pipe_kernel(DecodeArgs a, cons
   bool over = false;     // a stage max exceeded ref + kRefSlack
   bool fixed = false;    // second pass: ref = mmax of the first
 
-  // The score MFMAs of one stage (36), with the softmax work `work(g)` of the previous stage placed
-  // after each group g of four; operands are read two k-steps ahead.
+  // The score MFMAs of one stage (36 for 576-dim rows, 12 for 192-dim ones), with the softmax work
+  // `work(g)` of the previous stage placed after each group g of four; operands are read two k-steps
+  // ahead.
   auto scores = [&](const char* cur, floatx16& S, auto&& work) __attribute__((always_inline)) {
     int kl = klat0, kr = krope0;
     asm volatile("" : "+v"(kl), "+v"(kr));
@@ -234,7 +251,7 @@ __global__ __launch_bounds__(HB * 64) void decode_pipe_kernel(DecodeArgs a, cons
     ring[0] = s_operand(cur, 0, kl, kr);
     ring[1] = s_operand(cur, 1, kl, kr);
 #pragma unroll
-    for (int g = 0; g < C::KS / 4; ++g) {
+    for (int g = 0; g < C::NGS; ++g) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int k = 4 * g + j;
@@ -246,13 +263,13 @@ __global__ __launch_bounds__(HB * 64) void decode_pipe_kernel(DecodeArgs a, cons
     }
   };
 
-  // softmax of one stage's scores, in C::KS / 4 pieces (g = 0 .. KS/4 - 1); the state it leaves:
-  // pf (P^T fragments, bf16), and l_run / ref / mmax / over updated
+  // softmax of one stage's scores, in nine pieces (g = 0 .. 8: max, reference, four exp2 pieces, two
+  // bf16 packs, row sum); the state it leaves: pf (P^T fragments, bf16), and l_run / ref / mmax /
+  // over updated
   bf16x8_t pf[2];
   float sv[16], mt = 0.f;
   auto softmax_piece = [&](const floatx16& S, int g, bool first, bool last_stage, int stage0)
                            __attribute__((always_inline)) {
-    constexpr int G = C::KS / 4;
     if (g == 0) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) sv[i] = S[i];
@@ -281,7 +298,7 @@ __global__ __launch_bounds__(HB * 64) void decode_pipe_kernel(DecodeArgs a, cons
 #pragma unroll
       for (int j = 0; j < 8; ++j) f[j] = (__bf16)sv[8 + j];
       pf[1] = f;
-    } else if (g == G - 1) {
+    } else if (g == 8) {
       typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
       const bf16x2_t one2 = {(__bf16)1.f, (__bf16)1.f};
       float psum = 0.f;
@@ -293,7 +310,18 @@ __global__ __launch_bounds__(HB * 64) void decode_pipe_kernel(DecodeArgs a, cons
       l_run += psum + xor32(psum);
     }
   };
-  static_assert(C::KS / 4 == 9, "the softmax is laid out in nine pieces");
+  // the pieces that follow score group g: one each over nine groups; over three groups pieces 0-1,
+  // 2-5 and 6-8
+  auto softmax_group = [&](const floatx16& S, int g, bool first, bool last_stage, int stage0)
+                           __attribute__((always_inline)) {
+    if constexpr (C::NGS == 9) {
+      softmax_piece(S, g, first, last_stage, stage0);
+    } else {
+      const int lo = g == 0 ? 0 : (g == 1 ? 2 : 6), hi = g == 0 ? 2 : (g == 1 ? 6 : 9);
+#pragma unroll
+      for (int pc = lo; pc < hi; ++pc) softmax_piece(S, pc, first, last_stage, stage0);
+    }
+  };
 
   // O^T += V^T . P^T over all column blocks, in groups of four MFMAs (`work(g)` after group g); the
   // V operands are read two MFMAs ahead
@@ -365,19 +393,17 @@ __global__ __launch_bounds__(HB * 64) void decode_pipe_kernel(DecodeArgs a, cons
         if (n + 1 < nstage) {
           wait_stage(n + 1);
           lds_barrier();
-          // the nine copies of stage n + 3 are spread over the iteration, one per two groups of MFMAs
-          // (five among the score MFMAs, four among the P.V MFMAs): a copy instruction holds up the
-          // wave that issues it, so they are paced rather than issued in a burst
+          // the copies of stage n + 3 are spread over the iteration (C::copy_after_score / pv)
           scores(nxt, Snext, [&](int g) {
-            softmax_piece(S, g, n == 0, false, stage0);
-            if (refill_now && (g & 1) == 0) copy_block(src, refill, g / 2);
+            softmax_group(S, g, n == 0, false, stage0);
+            if (refill_now && C::copy_after_score(g)) copy_block(src, refill, C::score_copy(g));
           });
         } else {
 #pragma unroll
-          for (int g = 0; g < C::KS / 4; ++g) softmax_piece(S, g, n == 0, true, stage0);
+          for (int g = 0; g < C::NGS; ++g) softmax_group(S, g, n == 0, true, stage0);
         }
         pv(cur, [&](int g) __attribute__((always_inline)) {
-          if (refill_now && (g & 1)) copy_block(src, refill, 5 + g / 2);
+          if (refill_now && C::copy_after_pv(g)) copy_block(src, refill, C::pv_copy(g));
         });
       };
       for (int n0 = 0; n0 < nstage; n0 += 4) {
@@ -402,7 +428,7 @@ __global__ __launch_bounds__(HB * 64) void decode_pipe_kernel(DecodeArgs a, cons
   const float lse_v = (ref + log2f(l_run)) * kLn2;
   if (nsplit == 1) {
     if (!valid) return;
-    const size_t orow = (size_t)b * a.rows + gs * a.heads_per_set + head_in_set;
+    const size_t orow = (size_t)b * a.rows + (size_t)(qi * a.heads_per_set + head_in_set) * G + branch;
     if (h == 0) a.lse[orow] = lse_v;
 #pragma unroll
     for (int k = 0; k < C::CB; ++k) {
@@ -449,24 +475,44 @@ __global__ __launch_bounds__(HB * 64) void decode_pipe_kernel(DecodeArgs a, cons
 
 }  // namespace
 
-// The pipelined kernel serves bf16 latent caches with one set of 128 heads (absorbed MLA) and one
-// query token per work group: returns hipError_t, or -1 when the shape is not its own.
-int launch_decode_pipe(const ld_problem& p, const DecodeArgs& a, void* stream) {
-  if (!decode_pipe_serves(p, a.nsets, a.hblocks)) return -1;
+// The pipelined kernel serves bf16 latent caches whose query set is 128 heads over one latent slice
+// and the rope key: absorbed MLA (one 512-dim slice) and MLRA (one work group per 128-dim branch, four
+// branches or one branch of a tensor-parallel share).  Launchers return hipError_t, or -1 when the
+// shape is not the kernel's.
+namespace {
+
+template <int DL, int G, int MINB>
+int run_pipe(const DecodeArgs& a, void* stream) {
   const int units8 = (a.max_units + 7) / 8 * 8;
-  hipLaunchKernelGGL((decode_pipe_kernel<512, 64, 4>), dim3(units8 * a.wg_per_unit), dim3(4 * kWaveSize), 0,
+  hipLaunchKernelGGL((decode_pipe_kernel<DL, 64, 4, G, MINB>), dim3(units8 * a.wg_per_unit), dim3(4 * kWaveSize), 0,
                      static_cast<hipStream_t>(stream), a, a.block_table);
   return (int)hipGetLastError();
 }
 
-bool decode_pipe_serves(const ld_problem& p, int nsets, int hblocks) {
-  return p.kv_dtype == LD_BF16 && p.q_dtype == LD_BF16 && p.variant == LD_VARIANT_MLA && p.d_latent == 512 &&
-         p.d_rope == 64 && nsets == 1 && hblocks == 4;
+}  // namespace
+
+int launch_decode_pipe(const ld_problem& p, const DecodeArgs& a, void* stream) {
+  if (!decode_pipe_serves(p, a.nsets, a.hblocks)) return -1;
+  if (p.variant == LD_VARIANT_MLA) return run_pipe<512, 1, 1>(a, stream);
+  return p.num_groups == 4 ? run_pipe<128, 4, 2>(a, stream) : run_pipe<128, 1, 2>(a, stream);
 }
 
-int decode_pipe_wgs_per_cu() {
-  static int cache[kMaxDevices] = {};
-  return occupancy_cached(cache, reinterpret_cast<const void*>(decode_pipe_kernel<512, 64, 4>), 4 * kWaveSize);
+bool decode_pipe_serves(const ld_problem& p, int nsets, int hblocks) {
+  if (p.kv_dtype != LD_BF16 || p.q_dtype != LD_BF16 || p.d_rope != 64 || nsets != 1 || hblocks != 4) return false;
+  if (p.variant == LD_VARIANT_MLA) return p.d_latent == 512;
+  return p.variant == LD_VARIANT_MLRA && p.d_latent == 128 && (p.num_groups == 4 || p.num_groups == 1);
+}
+
+int decode_pipe_wgs_per_cu(const ld_problem& p) {
+  static int cache[3][kMaxDevices] = {};
+  if (p.variant == LD_VARIANT_MLA)
+    return occupancy_cached(cache[0], reinterpret_cast<const void*>(decode_pipe_kernel<512, 64, 4, 1, 1>),
+                            4 * kWaveSize);
+  if (p.num_groups == 4)
+    return occupancy_cached(cache[1], reinterpret_cast<const void*>(decode_pipe_kernel<128, 64, 4, 4, 2>),
+                            4 * kWaveSize);
+  return occupancy_cached(cache[2], reinterpret_cast<const void*>(decode_pipe_kernel<128, 64, 4, 1, 2>),
+                          4 * kWaveSize);
 }
 
 }  // namespace ld

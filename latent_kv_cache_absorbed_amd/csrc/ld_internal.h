@@ -164,12 +164,13 @@ struct ProjArgs {
   int32_t m, heads, n, k;
 };
 int launch_head_projection(const ProjArgs& a, int out_bf16, void* stream);
-// The software-pipelined kernel (decode_pipe.hip) for bf16 absorbed MLA with 128 heads per work group:
-// whether it serves the shape, its launcher (hipError_t, or -1 when it does not serve the shape) and
-// how many of its work groups fit on one CU.
+// The software-pipelined kernel (decode_pipe.hip) for bf16 latent caches with 128 heads per work group
+// over one latent slice and the rope key (absorbed MLA; MLRA with four branches or one): whether it
+// serves the shape, its launcher (hipError_t, or -1 when it does not serve the shape) and how many of
+// its work groups fit on one CU.
 bool decode_pipe_serves(const ld_problem& p, int nsets, int hblocks);
 int launch_decode_pipe(const ld_problem& p, const DecodeArgs& a, void* stream);
-int decode_pipe_wgs_per_cu();
+int decode_pipe_wgs_per_cu(const ld_problem& p);
 // The kernel for fp8 latent caches (decode_pipe_fp8.hip): 256-dim latent groups with a 64-dim RoPE
 // key, 64 heads per group, one or two groups per work group.
 bool decode_pipe8_serves(const ld_problem& p, int nsets, int hblocks);
