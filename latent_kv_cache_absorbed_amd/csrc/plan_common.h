@@ -26,6 +26,34 @@ constexpr int kCachedLens = 16;  // page counts per lane of the searching wave k
 
 __device__ __forceinline__ int plan_clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
 
+// Inclusive scan over the 64 lanes of a fully active wave by DPP lane moves (VALU operands, no LDS
+// round trip): shifts by 1, 2, 4 and 8 lanes inside each 16-lane row give every lane its row's
+// prefix, then lane 15 of rows 0 and 2 is broadcast into rows 1 and 3, and lane 31 into rows 2 and
+// 3.  A lane with no source lane, or a row left out by the row mask, takes 0, so `op` must be
+// associative with 0 as its identity on the values it sees: sums and maxima of non-negative counts.
+template <typename Op>
+__device__ __forceinline__ int wave_scan_dpp(int v, Op op) {
+  v = op(v, __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, true));   // row_shr:1
+  v = op(v, __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, true));   // row_shr:2
+  v = op(v, __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, true));   // row_shr:4
+  v = op(v, __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, true));   // row_shr:8
+  v = op(v, __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false));  // row_bcast:15 into rows 1, 3
+  v = op(v, __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false));  // row_bcast:31 into rows 2, 3
+  return v;
+}
+// sum saturated at 2^30 (operands at most 2^30, so the unsigned sum cannot wrap)
+__device__ __forceinline__ int sat_add(int x, int y) { return (int)min((unsigned)x + (unsigned)y, 1u << 30); }
+// wave-wide results (uniform): saturated sum, maximum, plain sum of non-negative counts
+__device__ __forceinline__ int wave_sum_sat(int v) {
+  return __builtin_amdgcn_readlane(wave_scan_dpp(v, [](int x, int y) { return sat_add(x, y); }), 63);
+}
+__device__ __forceinline__ int wave_max(int v) {
+  return __builtin_amdgcn_readlane(wave_scan_dpp(v, [](int x, int y) { return max(x, y); }), 63);
+}
+__device__ __forceinline__ int wave_sum(int v) {
+  return __builtin_amdgcn_readlane(wave_scan_dpp(v, [](int x, int y) { return x + y; }), 63);
+}
+
 // Automatic chunk (tokens), or 0 with forced splits.  Called by all 64 lanes of one wave; every
 // lane returns the same value.  The smallest chunk is found by bisection on the page count (the
 // unit count only falls as the chunk grows; ceil(L / (k * page)) = ceil(ceil(L / page) / k)), with
@@ -56,18 +84,15 @@ __device__ __forceinline__ int plan_auto_chunk(const PlanArgs& a, int lane) {
     mx = max(mx, pb);
     sum = min(sum + pb, 1u << 30);
   }
-  for (int off = 32; off > 0; off >>= 1) {
-    mx = max(mx, (unsigned)__shfl_xor((int)mx, off));
-    sum = min(sum + (unsigned)__shfl_xor((int)sum, off), 1u << 30);
-  }
+  mx = (unsigned)wave_max((int)mx);
+  sum = (unsigned)wave_sum_sat((int)sum);
   auto count = [&](unsigned k) {  // units for a chunk of k pages, saturated at 2^30
     unsigned cnt = 0;
 #pragma unroll
     for (int j = 0; j < kCachedLens; ++j)
       if (j < kk) cnt += (pg[j] + k - 1) / k;
     for (int b = lane + 64 * kCachedLens; b < a.batch; b += 64) cnt = min(cnt + (pages_of(b) + k - 1) / k, 1u << 30);
-    for (int off = 32; off > 0; off >>= 1) cnt = min(cnt + (unsigned)__shfl_xor((int)cnt, off), 1u << 30);
-    return cnt;
+    return (unsigned)wave_sum_sat((int)cnt);
   };
   // sum_b ceil(P_b / k) >= sum_b P_b / k, so no k below ceil(sum / target) qualifies; for
   // balanced lengths that bound usually does
@@ -127,13 +152,8 @@ __device__ __forceinline__ SeqPlan plan_seq(const PlanArgs& a, int chunk, int b)
 // tasks by the first work group of its first unit, the unit record by the unit's first work group,
 // and the header, the entries of empty sequences (which have no unit) and the zeroed combine
 // arrival counters by work group 0.
-__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int t = __shfl_up(v, off);
-    if (lane >= off) v += t;
-  }
-  return v;
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  return wave_scan_dpp(v, [](int x, int y) { return x + y; });
 }
 
 __device__ __forceinline__ void fused_plan_unit(const DecodeArgs& a, int x, int xcd, int yy, int sb, int* u) {
@@ -158,18 +178,18 @@ __device__ __forceinline__ void fused_plan_unit(const DecodeArgs& a, int x, int 
     return plan_seq_len(P, chunk_, bb, raw);
   };
   const int chunk = plan_auto_chunk(P, lane);
+  // the plan of the first 64 sequences is kept; every later block of 64 is derived again where needed
+  const SeqPlan sp0 = seq(chunk, 0);
   int tn = 0, tc = 0, tm = 0;
   for (int base = 0; base < P.batch; base += 64) {
-    const SeqPlan sp = seq(chunk, base);
-    tn = min(tn + sp.n, 1 << 30);
-    tc = min(tc + sp.nc, 1 << 30);
+    const SeqPlan sp = base == 0 ? sp0 : seq(chunk, base);
+    tn = sat_add(tn, sp.n);
+    tc = sat_add(tc, sp.nc);
     tm += sp.mc;
   }
-  for (int off = 32; off > 0; off >>= 1) {
-    tn = min(tn + __shfl_xor(tn, off), 1 << 30);
-    tc = min(tc + __shfl_xor(tc, off), 1 << 30);
-    tm += __shfl_xor(tm, off);
-  }
+  tn = wave_sum_sat(tn);
+  tc = wave_sum_sat(tc);
+  tm = wave_sum(tm);
   const int nunits = min(tn, P.max_units);
   if (x == 0) {
     if (lane == 0) {
@@ -183,8 +203,8 @@ __device__ __forceinline__ void fused_plan_unit(const DecodeArgs& a, int x, int 
     int cn = 0, cc = 0;
     for (int base = 0; base < P.batch; base += 64) {
       const int b = base + lane;
-      const SeqPlan sp = seq(chunk, base);
-      const int in = wave_incl_scan(sp.n, lane), ic = wave_incl_scan(sp.nc, lane);
+      const SeqPlan sp = base == 0 ? sp0 : seq(chunk, base);
+      const int in = wave_incl_scan(sp.n), ic = wave_incl_scan(sp.nc);
       if (b < P.batch && sp.n == 0) {
         const int ftask = cc + ic - sp.nc;
         P.seqs[4 * b] = 0;
@@ -193,8 +213,8 @@ __device__ __forceinline__ void fused_plan_unit(const DecodeArgs& a, int x, int 
         P.seqs[4 * b + 3] = 1;
         if (ftask < P.max_tasks) reinterpret_cast<int4*>(P.tasks)[ftask] = make_int4(b, 0, cn + in, 0);
       }
-      cn += __shfl(in, 63);
-      cc += __shfl(ic, 63);
+      cn += __builtin_amdgcn_readlane(in, 63);
+      cc += __builtin_amdgcn_readlane(ic, 63);
     }
   }
   const int per = (nunits + 7) >> 3;
@@ -207,26 +227,26 @@ __device__ __forceinline__ void fused_plan_unit(const DecodeArgs& a, int x, int 
   int cn = 0, cc = 0, cm = 0;
   int b = -1, first = 0, ftask = 0, mi = 0, L = 0, ck = 1, n = 0, nc = 0, mc = 0;
   for (int base = 0; base < P.batch; base += 64) {
-    const SeqPlan sp = seq(chunk, base);
-    const int in = wave_incl_scan(sp.n, lane), ic = wave_incl_scan(sp.nc, lane), im = wave_incl_scan(sp.mc, lane);
+    const SeqPlan sp = base == 0 ? sp0 : seq(chunk, base);
+    const int in = wave_incl_scan(sp.n), ic = wave_incl_scan(sp.nc), im = wave_incl_scan(sp.mc);
     const int f = cn + in - sp.n;
     const unsigned long long hit = __ballot(base + lane < P.batch && unit >= f && unit < f + sp.n);
     if (hit) {
       const int src = __ffsll(hit) - 1;
       b = base + src;
-      first = __shfl(f, src);
-      ftask = __shfl(cc + ic - sp.nc, src);
-      mi = __shfl(cm + im - sp.mc, src);
-      L = __shfl(sp.L, src);
-      ck = __shfl(sp.ck, src);
-      n = __shfl(sp.n, src);
-      nc = __shfl(sp.nc, src);
-      mc = __shfl(sp.mc, src);
+      first = __builtin_amdgcn_readlane(f, src);
+      ftask = __builtin_amdgcn_readlane(cc + ic - sp.nc, src);
+      mi = __builtin_amdgcn_readlane(cm + im - sp.mc, src);
+      L = __builtin_amdgcn_readlane(sp.L, src);
+      ck = __builtin_amdgcn_readlane(sp.ck, src);
+      n = __builtin_amdgcn_readlane(sp.n, src);
+      nc = __builtin_amdgcn_readlane(sp.nc, src);
+      mc = __builtin_amdgcn_readlane(sp.mc, src);
       break;
     }
-    cn += __shfl(in, 63);
-    cc += __shfl(ic, 63);
-    cm += __shfl(im, 63);
+    cn += __builtin_amdgcn_readlane(in, 63);
+    cc += __builtin_amdgcn_readlane(ic, 63);
+    cm += __builtin_amdgcn_readlane(im, 63);
   }
   if (b < 0) {  // unreachable: the units are counted from the same lengths
     if (lane == 0) u[0] = -1;
