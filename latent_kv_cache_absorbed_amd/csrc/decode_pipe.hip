@@ -1,11 +1,13 @@
-// Software-pipelined decode kernel for the latent shapes whose whole query set fits one work group
-// of one wave per 32-head block (absorbed MLA: 128 heads over one 576-dim shared row), gfx950.
-// See include/latent_decode.h for the operation and its sources.
+// Software-pipelined decode kernel for the latent shapes whose query set over one latent slice fits
+// one work group of one wave per 32-head block, gfx950: absorbed MLA (128 heads over one 576-dim
+// shared row) and MLRA (128 heads over one 128-dim branch plus the shared 64-dim rope key, one work
+// group per branch).  See include/latent_decode.h for the operation and its sources.
 //
-// One wave per SIMD, each wave one block of 32 heads over all score and value dims:
+// Each wave is one block of 32 heads over all score and value dims.  For MLA (one wave per SIMD):
 //   Q (32 heads x 576 bf16)  144 VGPRs, loaded once per unit
 //   O (32 heads x 512 f32)   256 AGPRs, accumulated by the P.V MFMAs
 //   S (32 tokens x 32 heads)  16 VGPRs per stage, two stages live
+// (an MLRA branch: Q 48 VGPRs, O 64 AGPRs, two work groups per CU).
 // No wave shares scores with another, so the only work-group barrier is the one that recycles the
 // stage buffers.  Each wave runs its stages as a software pipeline: while the score MFMAs of stage
 // n+1 run, the wave computes the softmax of stage n between them, then issues the P.V MFMAs of stage
