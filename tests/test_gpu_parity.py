@@ -63,6 +63,14 @@ def test_mla_bf16_small_heads():
     _check(inp)
 
 
+@pytest.mark.parametrize("groups,heads", [(4, 112), (1, 100)])
+def test_mlra_bf16_partial_head_block(groups, heads):
+    # MLRA branches on the pipelined kernel with a partly filled last 32-head block: absent heads' query
+    # rows are neither read past the tensor nor written
+    inp = synth.make_inputs("mlra", 2, heads, groups, 128, 64, [300, 2100], scale=1 / math.sqrt(192), seed=18)
+    _check(inp)
+
+
 def test_mla_bf16_partial_head_block():
     # 112 heads: the 128-head work group holds 16 absent heads, whose query rows it must neither read
     # past the last sequence's rows nor let into the result
