@@ -647,7 +647,7 @@ int run(const DecodeArgs& a, void* stream) {
   X(KV_FP8, 256, 64, KIND_LATENT, 4, 1, 1) X(KV_FP8, 256, 64, KIND_LATENT, 1, 4, 2)            \
   /* one GLA group of 64 heads (a tensor-parallel share) */                                   \
   X(KV_BF16, 256, 64, KIND_LATENT, 1, 2, 2) X(KV_FP8, 256, 64, KIND_LATENT, 1, 2, 2)            \
-  /* MLRA-4 (two branches of 128 heads per work group), one branch */                         \
+  /* MLRA, two branches or one of 128 heads per work group (bf16 with 4 or 1 branches: pipe) */\
   X(KV_BF16, 128, 64, KIND_LATENT, 2, 4, 1) X(KV_BF16, 128, 64, KIND_LATENT, 1, 4, 1)          \
   X(KV_FP8, 128, 64, KIND_LATENT, 2, 4, 1) X(KV_FP8, 128, 64, KIND_LATENT, 1, 4, 1)            \
   /* small latent shapes: up to 32 heads per set */                                           \
