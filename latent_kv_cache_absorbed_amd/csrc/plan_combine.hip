@@ -140,7 +140,8 @@ struct PieceGroup {
   size_t blk_in_unit, blocks_per_unit, piece_off, pieces;
 };
 
-__device__ __forceinline__ PieceGroup piece_group(const DecodeArgs& a, int d_v, int pg) {
+// plane: the piece position (0..63) within the group, by default this thread's lane
+__device__ __forceinline__ PieceGroup piece_group(const DecodeArgs& a, int d_v, int pg, int plane = -1) {
   PieceGroup p;
   const int vals = a.part_bf16 ? 8 : 4;
   const int jn = 16 / vals;
@@ -152,7 +153,7 @@ __device__ __forceinline__ PieceGroup piece_group(const DecodeArgs& a, int d_v, 
   rest /= cbn;
   p.hb = rest % a.hblocks;
   p.gs = rest / a.hblocks;
-  p.lane = threadIdx.x & 63;
+  p.lane = plane >= 0 ? plane : (int)(threadIdx.x & 63);
   p.h = p.lane >> 5;
   p.head_in_set = p.hb * 32 + (p.lane & 31);
   p.blk_in_unit = (size_t)p.gs * a.hblocks + p.hb;
@@ -426,12 +427,18 @@ __global__ __launch_bounds__(kCombineThreads) void combine_ws_kernel(DecodeArgs 
   write_piece(a, d_v, p, b, mm.o, mm.finish());
 }
 
-// Batches of a few long sequences (many splits each): work group (x, b) merges piece group x of
-// sequence b in one launch.  Its kSeqWaves waves take the sequence's chunks of kCombineChunk splits
-// round-robin; a wave issues all loads of a chunk at once and folds the chunk into its running
-// state in one step.  The states then meet in LDS in two rounds (four waves fold four states each,
-// then the first wave folds those four) and the first wave writes the result.
+// Batches of a few long sequences (many splits each): work group (x, b) merges part x % kSeqLanes
+// (kSeqPos piece positions) of piece group x / kSeqLanes of sequence b in one launch, so that one
+// sequence's merge spreads over kSeqLanes times as many work groups as it has piece groups (256 for
+// one 128-head MLA row set: every CU).  Its kSeqWaves waves take the sequence's chunks of
+// kCombineChunk splits round-robin; the kSeqLanes lanes of a piece position (l, l + kSeqPos, ..)
+// fold one part of every chunk each, issuing that part's loads at once and folding them in one step,
+// and then merge their states.  The states of the waves then meet in LDS in two rounds (four waves
+// fold four states each, then the first wave folds those four) and the first wave writes the result.
 constexpr int kSeqWaves = 16;
+constexpr int kSeqLanes = 2;                          // lanes per piece position (4: no faster)
+constexpr int kSeqPart = kCombineChunk / kSeqLanes;   // splits of a chunk one lane folds
+constexpr int kSeqPos = 64 / kSeqLanes;               // piece positions per work group
 
 __global__ __launch_bounds__(kSeqWaves * 64) void combine_seq_kernel(DecodeArgs a, int d_v) {
   __shared__ float st_m[kSeqWaves][64], st_t[kSeqWaves][64], st_o[kSeqWaves][8][64];
@@ -442,26 +449,30 @@ __global__ __launch_bounds__(kSeqWaves * 64) void combine_seq_kernel(DecodeArgs 
   const int n = max(0, min(n_all, a.max_units - first));
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
-  const PieceGroup p = piece_group(a, d_v, blockIdx.x);
+  const int part = lane / kSeqPos;  // which part of each chunk this lane folds
+  const PieceGroup p = piece_group(a, d_v, blockIdx.x / kSeqLanes,
+                                   (blockIdx.x % kSeqLanes) * kSeqPos + lane % kSeqPos);
   Merge m;
   for (int c0 = wave * kCombineChunk; c0 < n; c0 += kSeqWaves * kCombineChunk) {
-    const int cnt = min(n - c0, kCombineChunk);
-    // every load of the chunk is issued before any is used (raw pieces: 16 bytes each)
-    float ls[kCombineChunk];
-    uint4 raw[kCombineChunk];
+    const int s0 = c0 + part * kSeqPart;
+    const int cnt = min(n - s0, kSeqPart);  // none for the later parts of a short last chunk
+    if (cnt <= 0) continue;
+    // every load of the part is issued before any is used (raw pieces: 16 bytes each)
+    float ls[kSeqPart];
+    uint4 raw[kSeqPart];
 #pragma unroll
-    for (int k = 0; k < kCombineChunk; ++k) {
-      const size_t s = first + c0 + min(k, cnt - 1);
-      ls[k] = a.part_lse[(s * p.blocks_per_unit + p.blk_in_unit) * 32 + (lane & 31)];
+    for (int k = 0; k < kSeqPart; ++k) {
+      const size_t s = first + s0 + min(k, cnt - 1);
+      ls[k] = a.part_lse[(s * p.blocks_per_unit + p.blk_in_unit) * 32 + (p.lane & 31)];
       const size_t off = (s * p.blocks_per_unit + p.blk_in_unit) * (size_t)(32 * d_v) + p.piece_off;
       raw[k] = a.part_bf16 ? *reinterpret_cast<const uint4*>(static_cast<const __bf16*>(a.part_out) + off)
                            : *reinterpret_cast<const uint4*>(static_cast<const float*>(a.part_out) + off);
     }
-    // one online-merge step over the whole chunk, each piece converted as it is folded in
+    // one online-merge step over the part chunk, each piece converted as it is folded in
     float bm = -INFINITY;
     bool nan = false;
 #pragma unroll
-    for (int k = 0; k < kCombineChunk; ++k)
+    for (int k = 0; k < kSeqPart; ++k)
       if (k < cnt) {
         bm = fmaxf(bm, ls[k]);
         nan |= ls[k] != ls[k];
@@ -474,7 +485,7 @@ __global__ __launch_bounds__(kSeqWaves * 64) void combine_seq_kernel(DecodeArgs 
 #pragma unroll
       for (int e = 0; e < 8; ++e) m.o[e] *= r;
 #pragma unroll
-      for (int k = 0; k < kCombineChunk; ++k) {
+      for (int k = 0; k < kSeqPart; ++k) {
         const float w = k < cnt ? wexp(ls[k] - Mn) : 0.f;
         m.tot += w;
         const uint4 x = raw[k];
@@ -492,6 +503,16 @@ __global__ __launch_bounds__(kSeqWaves * 64) void combine_seq_kernel(DecodeArgs 
       }
       m.M = Mn;
     }
+  }
+  // the parts of this piece position's chunks (lanes l, l ^ kSeqPos, ..) meet; the lanes of the
+  // first part carry the result on
+#pragma unroll
+  for (int off = 32; off >= kSeqPos; off >>= 1) {
+    float o2[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o2[e] = __shfl_xor(m.o[e], off);
+    const float M2 = __shfl_xor(m.M, off), t2 = __shfl_xor(m.tot, off);
+    m.merge(M2, t2, o2);
   }
   st_m[wave][lane] = m.M;
   st_t[wave][lane] = m.tot;
@@ -520,7 +541,7 @@ __global__ __launch_bounds__(kSeqWaves * 64) void combine_seq_kernel(DecodeArgs 
     for (int e = 0; e < 8; ++e) st_o[wave][e][lane] = m.o[e];
   }
   __syncthreads();
-  if (wave != 0) return;
+  if (wave != 0 || part != 0) return;
   fold(1);
   fold(2);
   fold(3);
@@ -589,7 +610,7 @@ int launch_combine_ws(const DecodeArgs& a, int32_t d_v, void* stream) {
   if (a.batch <= kSeqCombineMaxBatch) {
     // a few sequences, so (when split) many splits each: one launch, one wide work group per
     // (piece group, sequence)
-    hipLaunchKernelGGL(combine_seq_kernel, dim3(a.xblocks * 4, a.batch), dim3(kSeqWaves * 64), 0,
+    hipLaunchKernelGGL(combine_seq_kernel, dim3(a.xblocks * 4 * kSeqLanes, a.batch), dim3(kSeqWaves * 64), 0,
                        static_cast<hipStream_t>(stream), a, d_v);
     return (int)hipGetLastError();
   }
