@@ -146,8 +146,8 @@ __global__ __launch_bounds__(HB * 64, MINB) void decode_pipe_kernel(DecodeArgs a
   // 512-dim slice, 2 for a 128-dim one), copy LPW the rope block.  The stage's rows come from one
   // page: its id is read from LDS once per stage.
   struct StageSrc {
-    const char* rows;
-    int tlast;
+    const char* rows;  // the stage's first cached row
+    int tlast;         // last valid row of the stage (rows past it repeat it)
   };
   auto stage_src = [&](int stage0) -> StageSrc {
     const int pi = stage0 / page_size - first_page;
@@ -155,9 +155,30 @@ __global__ __launch_bounds__(HB * 64, MINB) void decode_pipe_kernel(DecodeArgs a
     const size_t r0 = (size_t)page * page_size + (stage0 % page_size);
     return StageSrc{kbase + r0 * (size_t)grow_bytes, t_end - 1 - stage0};
   };
+  // Latent copies of 1 KB rows (MLA) take few instructions.  Copy j holds stage row q = wave + 4 j,
+  // and lane ln lands its chunk ln ^ swz_key(q).  For these q, swz_key(q) = kw ^ kj(j): bits 1 and 2
+  // are q's two low bits (the wave), bit 3 is the wave's bit 0 XOR j's bit 1, and bit 0 is
+  // j ^ (j >> 1)'s bit 0.  So the key is a scalar, and so is the source row min(q, tlast).  Per lane
+  // that leaves one XOR and one shift-add.  The key is passed through an empty asm, so the per-lane
+  // offsets depend on a value made inside the loop and are not hoisted into registers held across it.
+  constexpr bool kFastRows = C::LW == 1024 && C::WAVES == 4 && C::LPW == 8;
+  const int kw = ((wave & 1) << 1) | (((wave >> 1) & 1) << 2) | ((wave & 1) << 3);
   auto copy_block = [&](const StageSrc& src, char* buf, int j) __attribute__((always_inline)) {
-    // the per-lane offsets are derived from the lane index afresh (the empty asm hides that they are
-    // loop invariant), so they do not hold registers across the loop
+    if constexpr (kFastRows) {
+      if (j < C::LPW) {
+        const int q = wave + 4 * j;
+        int key = kw ^ (((j ^ (j >> 1)) & 1) | (((j >> 1) & 1) << 3));
+        asm volatile("" : "+s"(key));
+        const int row = min(q, src.tlast);
+        const unsigned voff = ((unsigned)(lane ^ key) << 4) + (unsigned)(row * C::GROW + lat_col);
+        const unsigned lbuf = (unsigned)(uintptr_t)(__attribute__((address_space(3))) char*)buf;
+        dma16_asm_at(src.rows, voff, lbuf + (unsigned)(q * 1024));
+        return;
+      }
+    }
+    // the general form (any row size; the rope block): the per-lane offsets are derived from the
+    // lane index afresh (the empty asm hides that they are loop invariant), so they do not hold
+    // registers across the loop
     int ln = lane;
     asm volatile("" : "+v"(ln));
     if (j < C::LPW) {
