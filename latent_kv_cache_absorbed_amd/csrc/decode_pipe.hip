@@ -139,6 +139,7 @@ __global__ __launch_bounds__(HB * 64, MINB) void decode_pipe_kernel(DecodeArgs a
   __syncthreads();
 
   const int grow_bytes = C::GROW;
+  const size_t page_bytes = (size_t)page_size * C::GROW;
   const int lat_col = branch * (DL * 2);  // byte offset of the work group's latent slice in a cached row
   const char* kbase = static_cast<const char*>(a.k);
   // Stage copies.  Wave w copies 1 KB blocks w, w + 4, .. of the latent region and block w of the
@@ -155,28 +156,58 @@ __global__ __launch_bounds__(HB * 64, MINB) void decode_pipe_kernel(DecodeArgs a
     const size_t r0 = (size_t)page * page_size + (stage0 % page_size);
     return StageSrc{kbase + r0 * (size_t)grow_bytes, t_end - 1 - stage0};
   };
-  // Latent copies of 1 KB rows (MLA) take few instructions.  Copy j holds stage row q = wave + 4 j,
-  // and lane ln lands its chunk ln ^ swz_key(q).  For these q, swz_key(q) = kw ^ kj(j): bits 1 and 2
-  // are q's two low bits (the wave), bit 3 is the wave's bit 0 XOR j's bit 1, and bit 0 is
-  // j ^ (j >> 1)'s bit 0.  So the key is a scalar, and so is the source row min(q, tlast).  Per lane
-  // that leaves one XOR and one shift-add.  The key is passed through an empty asm, so the per-lane
+  // Stage copies in few instructions.  The source row of a copy lane is min(token, tlast) (rows
+  // past a unit's end repeat its last row) and its LDS chunk is the lane's chunk XORed with
+  // swz_key(token); for the row sizes below the key splits into a part fixed by the copy (a scalar)
+  // and a part fixed by the lane.  The scalar part passes through an empty asm, so the per-lane
   // offsets depend on a value made inside the loop and are not hoisted into registers held across it.
-  constexpr bool kFastRows = C::LW == 1024 && C::WAVES == 4 && C::LPW == 8;
+  //  - 1 KB latent rows (MLA): copy j holds stage row q = wave + 4 j; lane ln lands chunk
+  //    ln ^ swz_key(q), and swz_key(q) = kw ^ kj: bits 1 and 2 are q's two low bits (the wave), bit 3
+  //    is the wave's bit 0 XOR j's bit 1, bit 0 is bit 0 of j ^ (j >> 1).
+  //  - 256-byte latent rows (an MLRA branch): copy j holds rows 4 q .. 4 q + 3 (q = wave + 4 j), 16
+  //    lanes a row; lane ln has row r = ln / 16 and lands chunk (ln % 16) ^ swz_key(4 q + r), where
+  //    swz_key(4 q + r) = kq(q) ^ kr(r) (kq: bit 0 = bit 0 of q ^ (q >> 1), bit 3 = q's bit 1;
+  //    kr: bits 1 and 3 = r's bit 0, bit 2 = r's bit 1).
+  //  - 128-byte rope rows: the wave's block holds rows 8 wave .. 8 wave + 7, 8 lanes a row; lane ln
+  //    has row r = ln / 8 and lands chunk (ln % 8) ^ (swz_key(8 wave + r) & 7), whose three bits are
+  //    r rotated left by one, bit 0 XORed with the wave's bit 0.
+  constexpr bool kFastLat1K = C::LW == 1024 && C::WAVES == 4;
+  constexpr bool kFastLat256 = C::LW == 256 && C::WAVES == 4;
+  constexpr bool kFastRope = C::RW == 128 && C::WAVES == 4;
   const int kw = ((wave & 1) << 1) | (((wave >> 1) & 1) << 2) | ((wave & 1) << 3);
+  const int r16 = lane >> 4;
+  const int c16 = (lane & 15) ^ (((r16 & 1) << 1) | (((r16 >> 1) & 1) << 2) | ((r16 & 1) << 3));
   auto copy_block = [&](const StageSrc& src, char* buf, int j) __attribute__((always_inline)) {
-    if constexpr (kFastRows) {
-      if (j < C::LPW) {
-        const int q = wave + 4 * j;
+    const unsigned lbuf = (unsigned)(uintptr_t)(__attribute__((address_space(3))) char*)buf;
+    if (j < C::LPW) {
+      const int q = wave + 4 * j;
+      if constexpr (kFastLat1K) {
         int key = kw ^ (((j ^ (j >> 1)) & 1) | (((j >> 1) & 1) << 3));
         asm volatile("" : "+s"(key));
         const int row = min(q, src.tlast);
         const unsigned voff = ((unsigned)(lane ^ key) << 4) + (unsigned)(row * C::GROW + lat_col);
-        const unsigned lbuf = (unsigned)(uintptr_t)(__attribute__((address_space(3))) char*)buf;
         dma16_asm_at(src.rows, voff, lbuf + (unsigned)(q * 1024));
         return;
       }
+      if constexpr (kFastLat256) {
+        int kq = ((q ^ (q >> 1)) & 1) | (((q >> 1) & 1) << 3);
+        asm volatile("" : "+s"(kq));
+        const int row = min(4 * q + r16, src.tlast);
+        const unsigned voff = __umul24((unsigned)row, (unsigned)C::GROW) + (unsigned)(lat_col + ((c16 ^ kq) << 4));
+        dma16_asm_at(src.rows, voff, lbuf + (unsigned)(q * 1024));
+        return;
+      }
+    } else if constexpr (kFastRope) {
+      int wb = wave & 1;
+      asm volatile("" : "+s"(wb));
+      const int r = lane >> 3;
+      const int row = min(8 * wave + r, src.tlast);
+      const int c = (lane & 7) ^ (((r << 1) | (r >> 2)) & 7) ^ wb;
+      const unsigned voff = __umul24((unsigned)row, (unsigned)C::GROW) + (unsigned)(C::ROPE_COL + (c << 4));
+      dma16_asm_at(src.rows, voff, lbuf + (unsigned)(C::ROPE_OFF + wave * 1024));
+      return;
     }
-    // the general form (any row size; the rope block): the per-lane offsets are derived from the
+    // the general form (other row sizes): the per-lane offsets are derived from the
     // lane index afresh (the empty asm hides that they are loop invariant), so they do not hold
     // registers across the loop
     int ln = lane;
@@ -265,21 +296,23 @@ __global__ __launch_bounds__(HB * 64, MINB) void decode_pipe_kernel(DecodeArgs a
   bool fixed = false;    // second pass: ref = mmax of the first
 
   // The score MFMAs of one stage (36 for 576-dim rows, 12 for 192-dim ones), with the softmax work
-  // `work(g)` of the previous stage placed after each group g of four; operands are read two k-steps
-  // ahead.
+  // `work(g)` of the previous stage placed after each group g of four; operands are read four k-steps
+  // ahead through a ring of five registers (two ahead measured 2% slower: the LDS latency under the
+  // stage copies exceeds two MFMAs).
+  constexpr int kScoreAhead = 4, kScoreRing = 5;
   auto scores = [&](const char* cur, floatx16& S, auto&& work) __attribute__((always_inline)) {
     int kl = klat0, kr = krope0;
     asm volatile("" : "+v"(kl), "+v"(kr));
-    bf16x8_t ring[4];
-    ring[0] = s_operand(cur, 0, kl, kr);
-    ring[1] = s_operand(cur, 1, kl, kr);
+    bf16x8_t ring[kScoreRing];
+#pragma unroll
+    for (int k = 0; k < kScoreAhead; ++k) ring[k] = s_operand(cur, k, kl, kr);
 #pragma unroll
     for (int g = 0; g < C::NGS; ++g) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int k = 4 * g + j;
-        if (k + 2 < C::KS) ring[(k + 2) & 3] = s_operand(cur, k + 2, kl, kr);
-        S = M::mma(ring[k & 3], qf[k], k == 0 ? floatx16{} : S);
+        if (k + kScoreAhead < C::KS) ring[(k + kScoreAhead) % kScoreRing] = s_operand(cur, k + kScoreAhead, kl, kr);
+        S = M::mma(ring[k % kScoreRing], qf[k], k == 0 ? floatx16{} : S);
       }
       work(g);
       __builtin_amdgcn_sched_barrier(0);
@@ -300,9 +333,11 @@ __global__ __launch_bounds__(HB * 64, MINB) void decode_pipe_kernel(DecodeArgs a
 #pragma unroll
         for (int i = 0; i < 16; ++i) sv[i] = (stage0 + M::token_of(i, h) < t_end) ? sv[i] : -INFINITY;
       }
-      mt = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])), fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
-      mt = fmaxf(mt, fmaxf(fmaxf(fmaxf(sv[8], sv[9]), fmaxf(sv[10], sv[11])),
-                           fmaxf(fmaxf(sv[12], sv[13]), fmaxf(sv[14], sv[15]))));
+      // maximum (NaN-propagating) is one v_maximum3_f32 per two values; fmaxf would first quieten
+      // every MFMA result with an extra v_max.  A NaN score makes its head's row NaN either way.
+      mt = sv[0];
+#pragma unroll
+      for (int i = 1; i < 16; ++i) mt = __builtin_elementwise_maximum(mt, sv[i]);
     } else if (g == 1) {
       mt = fmaxf(mt, xor32(mt)) * c2;
       if (!fixed && first) ref = mt;
@@ -408,11 +443,22 @@ __global__ __launch_bounds__(HB * 64, MINB) void decode_pipe_kernel(DecodeArgs a
       floatx16 SA, SB;
       scores(lds_b0, SA, [](int) {});
       // iteration n: scores of stage n+1 with the softmax of stage n between them, then P.V of n
+      // the stage refilled in iteration n is n + 3: its page (index into lds_pages) and its first
+      // token's offset in that page, advanced one stage per iteration (a page holds whole stages)
+      int rf_pi = (t_begin + 3 * kTile) / page_size - first_page;
+      int rf_off = (t_begin + 3 * kTile) % page_size;
       auto iter = [&](int n, floatx16& S, floatx16& Snext, char* cur, char* nxt, char* refill)
                       __attribute__((always_inline)) {
         const int stage0 = t_begin + n * kTile;
         const bool refill_now = n + 3 < nstage;
-        const StageSrc src = stage_src(t_begin + (n + 3) * kTile);
+        const int rf_page = __builtin_amdgcn_readfirstlane(lds_pages[min(rf_pi, kUnitPages - 1)]);
+        const StageSrc src{kbase + (size_t)rf_page * page_bytes + (size_t)(rf_off * grow_bytes),
+                           t_end - 1 - (stage0 + 3 * kTile)};
+        rf_off += kTile;
+        if (rf_off >= page_size) {
+          rf_off = 0;
+          ++rf_pi;
+        }
         if (n + 1 < nstage) {
           wait_stage(n + 1);
           lds_barrier();
