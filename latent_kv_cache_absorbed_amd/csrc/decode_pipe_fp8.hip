@@ -170,31 +170,44 @@ __global__ __launch_bounds__(G * 256) void decode_pipe8_kernel(DecodeArgs a, con
     return StageSrc{(size_t)page * page_size + (stage0 % page_size), t_end - 1 - stage0};
   };
   // Copy j of a wave's share of a stage (see P8Cfg): code blocks, then rope blocks, then (consumers)
-  // the 128 bytes of scales (lanes 0..7).  A stage's rows lie in one page.
+  // the 128 bytes of scales (lanes 0..7).  A stage's rows lie in one page.  The source row of a lane
+  // is min(token, tlast) (rows past a unit's end repeat its last row), and its LDS chunk is its
+  // chunk XORed with the row's key, which splits into a part fixed by the copy (a scalar, passed
+  // through an empty asm so that the per-lane offsets are made inside the loop, not held across it)
+  // and a part fixed by the lane:
+  //  - code rows of 256 bytes (one group): block q holds rows 4 q .. 4 q + 3, 16 lanes a row; lane ln
+  //    has row r = ln / 16 and chunk ln % 16, and ckey(4 q + r) = (r << 1) ^ ((q & 1) << 3) ^ (q >> 1 & 1);
+  //  - code rows of 512 bytes (two groups): block q holds rows 2 q, 2 q + 1, 32 lanes a row; lane ln
+  //    has row r = ln / 32 and chunk ln % 32 (the key touches its low four bits), and
+  //    ckey(2 q + r) = (r << 1) ^ ((q & 3) << 2) ^ (q >> 2 & 1);
+  //  - rope rows of 128 bytes: block q holds rows 8 q .. 8 q + 7, 8 lanes a row; lane ln has row
+  //    r = ln / 8, and swz_key(8 q + r) & 7 is r rotated left by one, bit 0 XORed with q's bit 0.
+  constexpr int RPB = 1024 / C::CROW;  // code rows per 1 KB block
+  static_assert(RPB == 4 || RPB == 2, "code rows of 256 or 512 bytes");
+  const int crow_r = lane / (C::CROW / 16);
+  const int crow_c = (lane % (C::CROW / 16)) ^ (crow_r << 1);
   auto copy_block = [&](const StageSrc& src, unsigned buf, int j) __attribute__((always_inline)) {
-    int ln = lane;
-    asm volatile("" : "+v"(ln));  // re-derived per copy, so the offsets hold no registers across the loop
     const int ncode = producer ? C::CODE_P : C::CODE_C;
     const int nrope = producer ? C::ROPE_P : C::ROPE_C;
     if (j < ncode) {
       const int q = (producer ? C::ROLE * C::CODE_C : 0) + rw + C::ROLE * j;
-      const int t = (q * 1024 + ln * 16) / C::CROW;
-      const int slot = ((q * 1024 + ln * 16) % C::CROW) >> 4;
-      const int c = (slot & 15) ^ ckey(t);
-      const int tu = min((q * 1024) / C::CROW, src.tlast);
-      unsigned voff = (unsigned)((min(t, src.tlast) - tu) * grow + (slot & ~15) * 16 + c * 16);
-      asm volatile("" : "+v"(voff));
-      dma16_asm_at(kbase + (src.r0 + tu) * (size_t)grow + lset0 * C::DL, voff, lds_u + buf + q * 1024);
+      int kq = RPB == 4 ? (((q & 1) << 3) | ((q >> 1) & 1)) : (((q & 3) << 2) | ((q >> 2) & 1));
+      asm volatile("" : "+s"(kq));
+      const int row = min(RPB * q + crow_r, src.tlast);
+      const unsigned voff = __umul24((unsigned)row, (unsigned)grow) + (unsigned)((crow_c ^ kq) << 4);
+      dma16_asm_at(kbase + src.r0 * (size_t)grow + lset0 * C::DL, voff, lds_u + buf + q * 1024);
     } else if (j < ncode + nrope) {
       const int q = (producer ? C::ROLE * C::ROPE_C : 0) + rw + C::ROLE * (j - ncode);
-      const int t = q * (1024 / C::RW) + ln / (C::RW / 16);
-      const int c = (ln % (C::RW / 16)) ^ (swz_key(t) & C::MR);
-      const int tu = min(q * (1024 / C::RW), src.tlast);
-      unsigned voff = (unsigned)((min(t, src.tlast) - tu) * C::RW + c * 16);
-      asm volatile("" : "+v"(voff));
-      dma16_asm_at(rbase + (src.r0 + tu) * (size_t)C::RW, voff, lds_u + buf + C::ROPE_OFF + q * 1024);
-    } else if (ln < kTile * 4 / 16) {
-      dma16_asm_at(sbase + src.r0 * 4, (unsigned)(ln * 16), lds_u + buf + C::SC_OFF);
+      static_assert(C::RW == 128, "rope rows of 128 bytes");
+      int qb = q & 1;
+      asm volatile("" : "+s"(qb));
+      const int r = lane >> 3;
+      const int row = min(8 * q + r, src.tlast);
+      const int c = (lane & 7) ^ (((r << 1) | (r >> 2)) & 7) ^ qb;
+      const unsigned voff = (unsigned)((row << 7) + (c << 4));
+      dma16_asm_at(rbase + src.r0 * (size_t)C::RW, voff, lds_u + buf + C::ROPE_OFF + q * 1024);
+    } else if (lane < kTile * 4 / 16) {
+      dma16_asm_at(sbase + src.r0 * 4, (unsigned)(lane * 16), lds_u + buf + C::SC_OFF);
     }
   };
   auto copy_stage = [&](const StageSrc& src, unsigned buf) __attribute__((always_inline)) {
@@ -325,9 +338,11 @@ __global__ __launch_bounds__(G * 256) void decode_pipe8_kernel(DecodeArgs a, con
 #pragma unroll
           for (int i = 0; i < 16; ++i) sv[i] = (stage0 + M::token_of(i, h) < t_end) ? sv[i] : -INFINITY;
         }
-        mt = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])), fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
-        mt = fmaxf(mt, fmaxf(fmaxf(fmaxf(sv[8], sv[9]), fmaxf(sv[10], sv[11])),
-                             fmaxf(fmaxf(sv[12], sv[13]), fmaxf(sv[14], sv[15]))));
+        // maximum (NaN-propagating) is one v_maximum3_f32 per two values; a NaN score makes its
+        // head's row NaN either way
+        mt = sv[0];
+#pragma unroll
+        for (int i = 1; i < 16; ++i) mt = __builtin_elementwise_maximum(mt, sv[i]);
       } else if (g == 0) {
         mt = fmaxf(mt, xor32(mt)) * c2;
         if (!fixed && n == 0) ref = mt;
