@@ -3,7 +3,7 @@
 // include/latent_decode.h for the operation and its sources.
 //
 // One wave computes a 32-column tile n0 .. n0+31 of one head for every row m, two 32-row tiles at a
-// time.  Both operands are read straight from memory as MFMA fragments: the activation row m holds
+// time, as C^T tiles (weights as the A operand), so each lane stores four consecutive columns at once.  Both operands are read straight from memory as MFMA fragments: the activation row m holds
 // its K values contiguously and so does the weight row n (W[h] is stored [N, K]), so every lane
 // loads 16 contiguous bytes per k-step.  The weights, which dominate the bytes (H*N*K), are read
 // once per pair of row tiles; the operands of eight k-steps are loaded before their MFMAs issue.
@@ -65,8 +65,8 @@ __global__ __launch_bounds__(kProjThreads) void head_projection_kernel(ProjArgs 
 #pragma unroll
         for (int j = 0; j < kKChunk; ++j) {
           if (s0 + j < ke) {
-            acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f0[j], wf[j], acc0, 0, 0, 0);
-            if (two) acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f1[j], wf[j], acc1, 0, 0, 0);
+            acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[j], f0[j], acc0, 0, 0, 0);
+            if (two) acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[j], f1[j], acc1, 0, 0, 0);
           }
         }
       }
@@ -87,21 +87,26 @@ __global__ __launch_bounds__(kProjThreads) void head_projection_kernel(ProjArgs 
         }
       }
     }
-    // lane holds column n0 + col of rows mt + 8 (r / 4) + 4 hh + r % 4 (and 32 further for acc1)
+    // C^T tiles (the weight rows are the A operand): lane holds row m = mt + col (32 further for acc1)
+    // and columns n0 + 8 (r / 4) + 4 hh + r % 4, so four consecutive registers are four consecutive
+    // columns of one output row, written by one 8-byte (bf16) or 16-byte (f32) store
     if (live && kq == 0) {
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         if (t == 1 && !two) break;
+        const int m = mt + 32 * t + col;
+        if (m < a.m) {
+          const floatx16& acc = t == 0 ? acc0 : acc1;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int m = mt + 32 * t + 8 * (r >> 2) + 4 * hh + (r & 3);
-          if (m < a.m) {
-            const float v = t == 0 ? acc0[r] : acc1[r];
-            const size_t o = ((size_t)m * a.heads + h) * a.n + n0 + col;
-            if constexpr (OUT_BF16)
-              static_cast<__bf16*>(a.c)[o] = (__bf16)v;
-            else
-              static_cast<float*>(a.c)[o] = v;
+          for (int g = 0; g < 4; ++g) {
+            const size_t o = ((size_t)m * a.heads + h) * a.n + n0 + 8 * g + 4 * hh;
+            if constexpr (OUT_BF16) {
+              *reinterpret_cast<bf16x4_t*>(static_cast<__bf16*>(a.c) + o) =
+                  bf16x4_t{(__bf16)acc[4 * g], (__bf16)acc[4 * g + 1], (__bf16)acc[4 * g + 2], (__bf16)acc[4 * g + 3]};
+            } else {
+              *reinterpret_cast<float4*>(static_cast<float*>(a.c) + o) =
+                  make_float4(acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]);
+            }
           }
         }
       }
