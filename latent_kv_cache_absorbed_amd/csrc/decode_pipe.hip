@@ -452,7 +452,10 @@ __global__ __launch_bounds__(HB * 64, MINB) void decode_pipe_kernel(DecodeArgs a
         const int stage0 = t_begin + n * kTile;
         const bool refill_now = n + 3 < nstage;
         const int rf_page = __builtin_amdgcn_readfirstlane(lds_pages[min(rf_pi, kUnitPages - 1)]);
-        const StageSrc src{kbase + (size_t)rf_page * page_bytes + (size_t)(rf_off * grow_bytes),
+        // (page ids are clamped to [0, num_pages) and a page's bytes fit in 32 bits: unsigned 32 x 32
+        // -> 64-bit products, no sign extension)
+        const StageSrc src{kbase + (uint64_t)(uint32_t)rf_page * (uint32_t)page_bytes +
+                               (uint32_t)rf_off * (uint32_t)grow_bytes,
                            t_end - 1 - (stage0 + 3 * kTile)};
         rf_off += kTile;
         if (rf_off >= page_size) {
