@@ -9,6 +9,8 @@
 // once per pair of row tiles; the operands of eight k-steps are loaded before their MFMAs issue.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+
 #include "decode_common.h"
 #include "ld_internal.h"
 
@@ -115,10 +117,103 @@ __global__ __launch_bounds__(kProjThreads) void head_projection_kernel(ProjArgs 
   }
 }
 
+// Staged form for k <= 512 (k % 64 == 0) and n % 64 == 0: a work group takes one head and 64 output
+// columns; it copies the 64 weight rows w[h, n0 .. n0 + 63, :] and 64 activation rows a[m0 .. m0 + 63,
+// h, :] whole into LDS with 1 KB global -> LDS copies (each row's 16-byte chunks land XOR-swizzled by
+// the row's three low bits: chunk c of row r sits in slot c ^ (r & 7), so the eight rows an MFMA
+// operand read touches in one cycle fall in distinct banks), then each of its four waves computes a
+// 32 x 32 C^T tile (columns 32 (wave & 1) .., rows 32 (wave >> 1) ..) from LDS.  One load burst per work
+// group, every byte fetched once by it; the weights stay in LDS across row tiles.
+template <int OUT_BF16>
+__global__ __launch_bounds__(kProjThreads) void head_projection_staged_kernel(ProjArgs a) {
+  extern __shared__ __attribute__((aligned(1024))) char smem[];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int nblocks = a.n / 64;
+  const int h = blockIdx.x / nblocks;
+  const int n0 = (blockIdx.x % nblocks) * 64;
+  const int RB = a.k * 2;                 // bytes of a row (all k)
+  const int region = 64 * RB;             // LDS bytes of 64 rows
+  char* const lw = smem;
+  char* const la = smem + region;
+  const int blocks = region / 1024;       // 1 KB copies per region
+  // copy q of a region (lane i): region bytes [1024 q + 16 i, +16) = row r, slot p; it holds chunk
+  // (p & ~7) | ((p & 7) ^ (r & 7)) of that row
+  auto copy_region = [&](char* dst, const char* base, size_t row_stride, int rows_valid) {
+    for (int q = wave; q < blocks; q += kProjThreads / 64) {
+      const int off = q * 1024 + lane * 16;
+      const int r = off / RB;
+      const int p = (off % RB) >> 4;
+      const int c = (p & ~7) | ((p & 7) ^ (r & 7));
+      const unsigned voff = (unsigned)((size_t)min(r, rows_valid - 1) * row_stride) + (unsigned)(c << 4);
+      dma16(base, voff, dst + q * 1024);
+    }
+  };
+  const char* wbase = static_cast<const char*>(a.w) + ((size_t)h * a.n + n0) * (size_t)RB;
+  copy_region(lw, wbase, (size_t)RB, 64);
+  const int wn = wave & 1, wm = wave >> 1;
+  const int col = lane & 31, hh = lane >> 5;
+  const int nr = 32 * wn + col;           // this lane's weight row (A operand row) in the region
+  for (int m0 = 0; m0 < a.m; m0 += 64) {
+    const char* abase = static_cast<const char*>(a.a) + ((size_t)m0 * a.heads + h) * (size_t)RB;
+    copy_region(la, abase, (size_t)a.heads * RB, min(64, a.m - m0));
+    __syncthreads();                      // every copy has landed
+    const int mr = 32 * wm + col;         // this lane's activation row (B operand column) in the region
+    floatx16 acc = floatx16{};
+    const int ksteps = a.k / 16;
+    for (int s = 0; s < ksteps; ++s) {
+      const int c = 2 * s + hh;           // chunk of k-step s held by this lane half
+      const bf16x8_t wf = __builtin_bit_cast(
+          bf16x8_t, *reinterpret_cast<const uint4*>(lw + nr * RB + (((c & ~7) | ((c & 7) ^ (nr & 7))) << 4)));
+      const bf16x8_t af = __builtin_bit_cast(
+          bf16x8_t, *reinterpret_cast<const uint4*>(la + mr * RB + (((c & ~7) | ((c & 7) ^ (mr & 7))) << 4)));
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf, af, acc, 0, 0, 0);
+    }
+    // C^T tile: lane holds row m0 + mr and columns n0 + 32 wn + 8 (r / 4) + 4 hh + r % 4
+    const int m = m0 + mr;
+    if (m < a.m) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const size_t o = ((size_t)m * a.heads + h) * a.n + n0 + 32 * wn + 8 * g + 4 * hh;
+        if constexpr (OUT_BF16) {
+          *reinterpret_cast<bf16x4_t*>(static_cast<__bf16*>(a.c) + o) =
+              bf16x4_t{(__bf16)acc[4 * g], (__bf16)acc[4 * g + 1], (__bf16)acc[4 * g + 2], (__bf16)acc[4 * g + 3]};
+        } else {
+          *reinterpret_cast<float4*>(static_cast<float*>(a.c) + o) =
+              make_float4(acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]);
+        }
+      }
+    }
+    __syncthreads();                      // the activation rows are rewritten for the next row tile
+  }
+}
+
 }  // namespace
 
 int launch_head_projection(const ProjArgs& a, int out_bf16, void* stream) {
   if (a.m == 0) return 0;
+  // staged form: k <= 512 (two 64-row regions of k * 2 bytes fit in LDS), 64-column blocks, and the
+  // activation rows of a 64-row tile addressable by 32-bit offsets from the tile's first row
+  if (a.k % 64 == 0 && a.k <= 512 && a.n % 64 == 0 && 64LL * a.heads * a.k * 2 < (1LL << 31)) {
+    const dim3 grid((unsigned)((long long)a.heads * (a.n / 64)));
+    const size_t lds = (size_t)2 * 64 * a.k * 2;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    // more than 64 KB of dynamic LDS needs the kernel's limit raised (once per process; a repeated
+    // call is harmless)
+    static std::atomic<bool> raised[2] = {false, false};
+    const void* f = out_bf16 ? reinterpret_cast<const void*>(head_projection_staged_kernel<1>)
+                             : reinterpret_cast<const void*>(head_projection_staged_kernel<0>);
+    if (lds > 65536 && !raised[out_bf16 ? 1 : 0].load(std::memory_order_relaxed)) {
+      const hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, 128 * 1024);
+      if (e != hipSuccess) return (int)e;
+      raised[out_bf16 ? 1 : 0].store(true, std::memory_order_relaxed);
+    }
+    if (out_bf16)
+      hipLaunchKernelGGL((head_projection_staged_kernel<1>), grid, dim3(kProjThreads), lds, s, a);
+    else
+      hipLaunchKernelGGL((head_projection_staged_kernel<0>), grid, dim3(kProjThreads), lds, s, a);
+    return (int)hipGetLastError();
+  }
   constexpr int WAVES = kProjThreads / 64;
   const long long tiles = (long long)a.heads * (a.n / 32);
   // a long k is split over the four waves of a work group (one tile each), a short one is not

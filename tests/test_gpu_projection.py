@@ -45,6 +45,7 @@ def _bf16(r, *shape, std=1.0):
 
 
 @pytest.mark.parametrize("m,H,n,k", [(64, 128, 512, 128), (64, 128, 128, 512), (1, 128, 512, 128),
+                                     (130, 4, 192, 256), (70, 3, 64, 64),
                                      (100, 3, 64, 48), (33, 5, 32, 16), (65, 2, 96, 400)])
 @pytest.mark.parametrize("out_dtype", ["bf16", "f32"])
 def test_projection(m, H, n, k, out_dtype):
