@@ -263,7 +263,9 @@ int32_t ld_cache_append(const ld_problem* p, const void* c_new, const void* kr_n
  * latent-projection kernel).
  *   a bf16 [m, heads, k]; w bf16 [heads, n, k] (row j of w[h] holds the k weights of output j);
  *   c [m, heads, n] in out_dtype (F32 or BF16, rounded to nearest even).  n a multiple of 32, k a
- *   multiple of 16, pointers 16-byte aligned.  m = 0 does nothing.  Asynchronous on `stream`. */
+ *   multiple of 16, pointers 16-byte aligned.  m = 0 does nothing.  Asynchronous on `stream`.  The first
+ *   call on a device with 256 < k <= 512 (k % 64 == 0, n % 64 == 0) also raises, once, the dynamic LDS
+ *   limit of the kernel that serves it (a host-side attribute; its failure is reported as LD_ERR_HIP). */
 int32_t ld_head_projection(int32_t m, int32_t heads, int32_t n, int32_t k, const void* a, const void* w, void* c,
                            int32_t out_dtype, void* stream);
 

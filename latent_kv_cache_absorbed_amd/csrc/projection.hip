@@ -198,15 +198,21 @@ int launch_head_projection(const ProjArgs& a, int out_bf16, void* stream) {
     const dim3 grid((unsigned)((long long)a.heads * (a.n / 64)));
     const size_t lds = (size_t)2 * 64 * a.k * 2;
     const hipStream_t s = static_cast<hipStream_t>(stream);
-    // more than 64 KB of dynamic LDS needs the kernel's limit raised (once per process; a repeated
-    // call is harmless)
-    static std::atomic<bool> raised[2] = {false, false};
+    // more than 64 KB of dynamic LDS needs the kernel's limit raised, once per kernel and device (a
+    // repeated call is harmless, so threads racing here are fine)
+    static std::atomic<bool> raised[2][kMaxDevices] = {};
     const void* f = out_bf16 ? reinterpret_cast<const void*>(head_projection_staged_kernel<1>)
                              : reinterpret_cast<const void*>(head_projection_staged_kernel<0>);
-    if (lds > 65536 && !raised[out_bf16 ? 1 : 0].load(std::memory_order_relaxed)) {
-      const hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, 128 * 1024);
-      if (e != hipSuccess) return (int)e;
-      raised[out_bf16 ? 1 : 0].store(true, std::memory_order_relaxed);
+    if (lds > 65536) {
+      int dev = 0;
+      const hipError_t ed = hipGetDevice(&dev);
+      if (ed != hipSuccess) return (int)ed;
+      std::atomic<bool>* flag = dev >= 0 && dev < kMaxDevices ? &raised[out_bf16 ? 1 : 0][dev] : nullptr;
+      if (!flag || !flag->load(std::memory_order_relaxed)) {
+        const hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, 128 * 1024);
+        if (e != hipSuccess) return (int)e;
+        if (flag) flag->store(true, std::memory_order_relaxed);
+      }
     }
     if (out_bf16)
       hipLaunchKernelGGL((head_projection_staged_kernel<1>), grid, dim3(kProjThreads), lds, s, a);
