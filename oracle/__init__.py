@@ -9,7 +9,9 @@ algebraic identities stated on the pages, brute force in 40-digit decimal
 arithmetic, and library routines (torch CPU fp64 attention, torch's float8
 decoder).  RoPE (``rope``) is the one part whose *flavour* the pages leave
 open; its invariants are pinned, its pair layout and base are a reading
-(parity unpinned for the flavour, and the GPU path never applies RoPE).
+(parity unpinned for the flavour and base).  The decode kernels never rotate;
+the GPU cache append rotates the new key under the same reading, so its
+parity test cannot catch a different flavour or base.
 """
 from .attention import *  # noqa: F401,F403
 from .cache import *  # noqa: F401,F403
